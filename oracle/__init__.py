@@ -1,0 +1,8 @@
+"""fp64 CPU oracle for multi-scale retention (test infrastructure only).
+
+Only tests, the package smoke check and the benchmark's CPU-baseline leg may
+import this package.  See ``retention_oracle`` for what it computes.
+"""
+from .retention_oracle import chunkwise, chunk_state_contribution, parallel, recurrent, recurrent_step
+
+__all__ = ["recurrent", "recurrent_step", "parallel", "chunkwise", "chunk_state_contribution"]

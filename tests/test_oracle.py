@@ -1,0 +1,348 @@
+"""Pins for the fp64 CPU oracle (no GPU).
+
+The oracle is checked against things other than itself: values worked by hand
+from the retention definition (tests/golden), a pure-Python brute force of the
+definition, closed forms (gamma = 0, gamma = 1), invariants the pages fix
+(equivalence of the forms, per-head independence, causality) and a
+mutation check showing that plausible slips in the recurrence fail a pin.
+
+Definition and forms: "Retentive Networks — Microsoft Propone l'Alternativa
+Architetturale ai Transformer" (aimpact page), section "Il meccanismo:
+Multi-Scale Retention".
+"""
+import json
+import math
+import os
+
+import pytest
+import torch
+
+import oracle
+from retnet_retention_chunkwise_amd.workloads import WORKLOADS, make_decode_inputs, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rel(a, b):
+    a = torch.as_tensor(a, dtype=torch.float64)
+    b = torch.as_tensor(b, dtype=torch.float64)
+    return float((a - b).norm() / b.norm().clamp_min(1e-300))
+
+
+def rand(B, H, T, dk, dv, seed=0, state=False):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, H, T, dk, generator=g, dtype=torch.float64)
+    k = torch.randn(B, H, T, dk, generator=g, dtype=torch.float64)
+    v = torch.randn(B, H, T, dv, generator=g, dtype=torch.float64)
+    s = torch.randn(B, H, dk, dv, generator=g, dtype=torch.float64) if state else None
+    return q, k, v, s
+
+
+# ---------------------------------------------------------------- hand values
+def _scalar_rows():
+    rows = []
+    with open(os.path.join(GOLDEN, "scalar_geometric.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                g, n, y = line.split()
+                rows.append((float(g), int(n), float(y)))
+    return rows
+
+
+@pytest.mark.parametrize("form", ["recurrent", "parallel", "chunk1", "chunk3", "chunk8"])
+def test_scalar_geometric_golden(form):
+    rows = _scalar_rows()
+    for gamma in sorted({r[0] for r in rows}):
+        want = {n: y for g, n, y in rows if g == gamma}
+        T = max(want) + 1
+        one = torch.ones(1, 1, T, 1, dtype=torch.float64)
+        gm = torch.tensor([gamma], dtype=torch.float64)
+        if form == "recurrent":
+            y, _ = oracle.recurrent(one, one, one, gm)
+        elif form == "parallel":
+            y = oracle.parallel(one, one, one, gm)
+        else:
+            y, _ = oracle.chunkwise(one, one, one, gm, int(form[5:]))
+        for n, val in want.items():
+            assert abs(float(y[0, 0, n, 0]) - val) <= 1e-12 * max(1.0, val), (form, gamma, n)
+
+
+@pytest.mark.parametrize("form", ["recurrent", "parallel", "chunk1", "chunk2", "chunk3"])
+def test_hand_example_golden(form):
+    ex = json.load(open(os.path.join(GOLDEN, "hand_example.json")))
+    Q = torch.tensor(ex["Q"], dtype=torch.float64)[None, None]
+    K = torch.tensor(ex["K"], dtype=torch.float64)[None, None]
+    V = torch.tensor(ex["V"], dtype=torch.float64)[None, None]
+    gm = torch.tensor([ex["gamma"]])
+    Y = torch.tensor(ex["Y"], dtype=torch.float64)
+    S = torch.tensor(ex["S_final"], dtype=torch.float64)
+    if form == "recurrent":
+        y, s = oracle.recurrent(Q, K, V, gm)
+    elif form == "parallel":
+        y, s = oracle.parallel(Q, K, V, gm), None
+    else:
+        y, s = oracle.chunkwise(Q, K, V, gm, int(form[5:]))
+    assert torch.equal(y[0, 0], Y)  # exact: all values are short binary fractions
+    if s is not None:
+        assert torch.equal(s[0, 0], S)
+
+
+# ------------------------------------------------- brute force of the definition
+def _definition_loops(q, k, v, gamma, s0):
+    """Y_n = sum_{m<=n} gamma^(n-m) (Q_n . K_m) V_m + gamma^(n+1) Q_n S0, in Python loops."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    out = torch.zeros(B, H, T, dv, dtype=torch.float64)
+    for b in range(B):
+        for h in range(H):
+            g = float(gamma[h])
+            for n in range(T):
+                for c in range(dv):
+                    acc = 0.0
+                    for m in range(n + 1):
+                        dot = sum(float(q[b, h, n, i]) * float(k[b, h, m, i]) for i in range(dk))
+                        acc += (g ** (n - m)) * dot * float(v[b, h, m, c])
+                    if s0 is not None:
+                        acc += (g ** (n + 1)) * sum(float(q[b, h, n, i]) * float(s0[b, h, i, c]) for i in range(dk))
+                    out[b, h, n, c] = acc
+    return out
+
+
+@pytest.mark.parametrize("with_state", [False, True])
+def test_pure_python_definition(with_state):
+    q, k, v, s0 = rand(1, 3, 9, 3, 4, seed=1, state=with_state)
+    gamma = torch.tensor([0.0, 0.6, 1.0])
+    want = _definition_loops(q, k, v, gamma, s0)
+    y_r, _ = oracle.recurrent(q, k, v, gamma, s0)
+    y_p = oracle.parallel(q, k, v, gamma, s0)
+    assert rel(y_r, want) < 1e-13
+    assert rel(y_p, want) < 1e-13
+    for C in (1, 2, 4, 9, 16):
+        y_c, _ = oracle.chunkwise(q, k, v, gamma, C, s0)
+        assert rel(y_c, want) < 1e-13, C
+
+
+# ------------------------------------------------------------- closed forms
+def test_gamma_zero_is_diagonal():
+    q, k, v, s0 = rand(2, 2, 11, 5, 6, seed=2, state=True)
+    gamma = torch.zeros(2)
+    want = (q * k).sum(-1, keepdim=True) * v          # Y_n = (Q_n . K_n) V_n
+    y, s = oracle.recurrent(q, k, v, gamma, s0)       # S_in decays away at once (gamma^(n+1) = 0)
+    assert rel(y, want) < 1e-14
+    assert rel(s, k[:, :, -1, :, None] * v[:, :, -1, None, :]) < 1e-14
+    for C in (1, 4, 11):
+        yc, sc = oracle.chunkwise(q, k, v, gamma, C, s0)
+        assert rel(yc, want) < 1e-14
+        assert rel(sc, s) < 1e-14
+
+
+def test_gamma_one_is_causal_linear_attention_without_denominator():
+    # gamma = 1: Y_n = Q_n sum_{m<=n} K_m^T V_m, a prefix sum of outer products
+    q, k, v, s0 = rand(1, 2, 13, 4, 3, seed=3, state=True)
+    gamma = torch.ones(2)
+    prefix = torch.cumsum(k.unsqueeze(-1) * v.unsqueeze(-2), dim=2) + s0.unsqueeze(2)
+    want = (q.unsqueeze(-1) * prefix).sum(-2)
+    y, s = oracle.recurrent(q, k, v, gamma, s0)
+    assert rel(y, want) < 1e-13
+    assert rel(s, prefix[:, :, -1]) < 1e-13
+    assert rel(oracle.parallel(q, k, v, gamma, s0), want) < 1e-13
+
+
+# ------------------------------------------------------------- invariants
+@pytest.mark.parametrize("C", [1, 2, 3, 4, 7, 16, 37, 64])
+def test_forms_equivalent_any_chunk_length(C):
+    q, k, v, s0 = rand(2, 3, 37, 8, 5, seed=4, state=True)
+    gamma = torch.tensor([0.3, 0.9, 1.0])
+    y_r, s_r = oracle.recurrent(q, k, v, gamma, s0)
+    y_c, s_c = oracle.chunkwise(q, k, v, gamma, C, s0)
+    assert rel(y_c, y_r) < 1e-12
+    assert rel(s_c, s_r) < 1e-12
+    assert rel(oracle.parallel(q, k, v, gamma, s0), y_r) < 1e-12
+
+
+def test_state_handoff_split():
+    q, k, v, s0 = rand(1, 2, 50, 6, 7, seed=5, state=True)
+    gamma = torch.tensor([0.8, 0.95])
+    y, s = oracle.recurrent(q, k, v, gamma, s0)
+    for t in (1, 17, 49):
+        y1, s1 = oracle.recurrent(q[:, :, :t], k[:, :, :t], v[:, :, :t], gamma, s0)
+        y2, s2 = oracle.chunkwise(q[:, :, t:], k[:, :, t:], v[:, :, t:], gamma, 8, s1)
+        assert rel(torch.cat([y1, y2], dim=2), y) < 1e-12
+        assert rel(s2, s) < 1e-12
+
+
+def test_decode_steps_equal_recurrent():
+    q, k, v, s0 = rand(3, 2, 12, 4, 6, seed=6, state=True)
+    gamma = torch.tensor([0.5, 0.99])
+    y, s = oracle.recurrent(q, k, v, gamma, s0)
+    S = s0
+    for n in range(12):
+        yn, S = oracle.recurrent_step(q[:, :, n], k[:, :, n], v[:, :, n], gamma, S)
+        assert rel(yn, y[:, :, n]) < 1e-13
+    assert rel(S, s) < 1e-13
+
+
+def test_heads_independent_and_permutable():
+    q, k, v, s0 = rand(2, 4, 20, 4, 4, seed=7, state=True)
+    gamma = torch.tensor([0.1, 0.5, 0.9, 1.0])
+    y, s = oracle.recurrent(q, k, v, gamma, s0)
+    perm = torch.tensor([2, 0, 3, 1])
+    yp, sp = oracle.recurrent(q[:, perm], k[:, perm], v[:, perm], gamma[perm], s0[:, perm])
+    assert torch.equal(yp, y[:, perm]) and torch.equal(sp, s[:, perm])
+    # changing one head leaves the others bit-identical
+    q2 = q.clone()
+    q2[:, 1] += 1.0
+    y2, _ = oracle.recurrent(q2, k, v, gamma, s0)
+    for h in (0, 2, 3):
+        assert torch.equal(y2[:, h], y[:, h])
+    assert not torch.equal(y2[:, 1], y[:, 1])
+
+
+def test_bilinear_and_causal():
+    q, k, v, _ = rand(1, 2, 16, 3, 5, seed=8)
+    gamma = torch.tensor([0.7, 0.95])
+    y, _ = oracle.recurrent(q, k, v, gamma)
+    assert rel(oracle.recurrent(2.5 * q, k, v, gamma)[0], 2.5 * y) < 1e-14
+    assert rel(oracle.recurrent(q, -3.0 * k, v, gamma)[0], -3.0 * y) < 1e-14
+    v2 = torch.randn_like(v)
+    ysum = oracle.recurrent(q, k, v + v2, gamma)[0]
+    assert rel(ysum, y + oracle.recurrent(q, k, v2, gamma)[0]) < 1e-13
+    # perturbing token t leaves rows < t unchanged and changes row t
+    t = 9
+    k3 = k.clone()
+    k3[:, :, t] += 1.0
+    y3, _ = oracle.recurrent(q, k3, v, gamma)
+    assert torch.equal(y3[:, :, :t], y[:, :, :t])
+    assert not torch.equal(y3[:, :, t], y[:, :, t])
+
+
+def test_negative_scores_not_clamped():
+    # Scores Q_n . K_m may be negative; no softmax, clamp or denominator.
+    q = torch.tensor([[[[1.0], [1.0]]]], dtype=torch.float64)
+    k = torch.tensor([[[[-2.0], [1.0]]]], dtype=torch.float64)
+    v = torch.tensor([[[[1.0], [1.0]]]], dtype=torch.float64)
+    y, _ = oracle.recurrent(q, k, v, torch.tensor([0.5]))
+    assert y[0, 0, 0, 0] == -2.0           # 1 * (-2) * 1
+    assert y[0, 0, 1, 0] == 0.0            # 0.5 * (-2) + 1
+
+
+def test_rsm_dense_router_special_case():
+    """Routing-slot-memory recurrence with a dense router reduces to retention.
+
+    "Raven: High-Recall Sequence Modeling with Sparse Memory Routing"
+    (gist.science page), section "2.1 Il Framework RSM": S_t = (1 - r_t) * S_(t-1)
+    + r_t * (D_t S_(t-1) A_t + U_t); an SSM uses the dense router r_t = 1.  With
+    D_t = gamma I, A_t = I and U_t = k_t^T v_t this is the retention recurrence.
+    """
+    q, k, v, s0 = rand(1, 1, 10, 3, 4, seed=9, state=True)
+    g = 0.85
+    S = s0[0, 0].clone()
+    r = torch.ones(3, 1, dtype=torch.float64)
+    D, A = g * torch.eye(3, dtype=torch.float64), torch.eye(4, dtype=torch.float64)
+    for t in range(10):
+        U = torch.outer(k[0, 0, t], v[0, 0, t])
+        S = (1 - r) * S + r * (D @ S @ A + U)
+    _, s = oracle.recurrent(q, k, v, torch.tensor([g], dtype=torch.float64), s0)
+    assert rel(S, s[0, 0]) < 1e-13
+
+
+# ----------------------------------------------- workloads feed the oracle
+def test_workload_inputs_are_exactly_representable():
+    wl = WORKLOADS["tiny"]
+    q, k, v = make_inputs(wl.B, wl.H, wl.T, wl.dk, wl.dv, wl.dtype, seed=0)
+    assert q.dtype == torch.float32 and q.shape == (1, 2, 64, 16)
+    q2, _, _ = make_inputs(wl.B, wl.H, wl.T, wl.dk, wl.dv, wl.dtype, seed=0)
+    assert torch.equal(q, q2)  # seeded and reproducible
+    qb, kb, vb = make_inputs(1, 2, 8, 16, 32, "bf16", seed=0)
+    assert qb.dtype == torch.bfloat16 and vb.shape == (1, 2, 8, 32)
+    assert torch.equal(qb.double().bfloat16(), qb)
+    dq, dk_, dv_, s0 = make_decode_inputs(2, 2, 16, 32, steps=3, seed=0)
+    assert dq.shape == (3, 2, 2, 16) and dv_.shape == (3, 2, 2, 32) and s0.dtype == torch.float32
+    # gamma schedules: 1 - 2^(-5-h) and 1 - 2^(-5-h/2)
+    assert WORKLOADS["layer1p3b"].gammas[0] == pytest.approx(1 - 2 ** -5)
+    assert WORKLOADS["layer6p7b"].gammas[3] == pytest.approx(1 - 2 ** -6.5, abs=1e-7)
+
+
+def test_tiny_workload_forms_agree():
+    wl = WORKLOADS["tiny"]
+    q, k, v = make_inputs(wl.B, wl.H, wl.T, wl.dk, wl.dv, wl.dtype, seed=0)
+    gamma = torch.tensor(wl.gammas)
+    y_r, s_r = oracle.recurrent(q, k, v, gamma)
+    y_c, s_c = oracle.chunkwise(q, k, v, gamma, wl.C)
+    assert rel(y_c, y_r) < 1e-13 and rel(s_c, s_r) < 1e-13
+    assert rel(oracle.parallel(q, k, v, gamma), y_r) < 1e-13
+
+
+# ------------------------------------------------------------- mutation check
+def _mutant(kind):
+    """Recurrent forms with one plausible slip each (planted here, on the CPU)."""
+
+    def run(q, k, v, gamma, state_in=None):
+        q, k, v = q.double(), k.double(), v.double()
+        B, H, T, dk = q.shape
+        dv = v.shape[-1]
+        g = torch.as_tensor(gamma, dtype=torch.float64).view(1, H, 1, 1)
+        if kind == "heads_reversed":
+            g = g.flip(1)
+        S = torch.zeros(B, H, dk, dv, dtype=torch.float64) if state_in is None else state_in.double().clone()
+        y = torch.empty(B, H, T, dv, dtype=torch.float64)
+        for n in range(T):
+            kv = k[:, :, n, :, None] * v[:, :, n, None, :]
+            if kind == "exclusive":          # Y_n = Q_n S_(n-1)
+                y[:, :, n] = torch.einsum("bhk,bhkv->bhv", q[:, :, n], S)
+                S = g * S + kv
+                continue
+            if kind == "decay_off_by_one":
+                S = g * (S + kv)
+            elif kind == "no_decay":
+                S = S + kv
+            elif kind == "minus":
+                S = g * S - kv
+            elif kind == "state_not_decayed" and n == 0:
+                S = S + kv
+            elif kind == "query_key_swapped":
+                S = g * S + q[:, :, n, :, None] * v[:, :, n, None, :]
+            else:
+                S = g * S + kv
+            qq = k[:, :, n] if kind == "query_key_swapped" else q[:, :, n]
+            y[:, :, n] = torch.einsum("bhk,bhkv->bhv", qq, S)
+        return y, S
+
+    return run
+
+
+def _pins_fail(fn):
+    """True if at least one pin rejects ``fn`` (a recurrent-form candidate)."""
+    try:
+        # hand example
+        ex = json.load(open(os.path.join(GOLDEN, "hand_example.json")))
+        Q = torch.tensor(ex["Q"], dtype=torch.float64)[None, None]
+        K = torch.tensor(ex["K"], dtype=torch.float64)[None, None]
+        V = torch.tensor(ex["V"], dtype=torch.float64)[None, None]
+        y, s = fn(Q, K, V, torch.tensor([ex["gamma"]]))
+        if not torch.equal(y[0, 0], torch.tensor(ex["Y"], dtype=torch.float64)):
+            return True
+        # brute force with a state and distinct per-head gammas
+        q, k, v, s0 = rand(1, 3, 7, 3, 4, seed=11, state=True)
+        gamma = torch.tensor([0.0, 0.6, 1.0])
+        if rel(fn(q, k, v, gamma, s0)[0], _definition_loops(q, k, v, gamma, s0)) > 1e-12:
+            return True
+        # scalar geometric
+        for g, n, val in _scalar_rows():
+            one = torch.ones(1, 1, n + 1, 1, dtype=torch.float64)
+            if abs(float(fn(one, one, one, torch.tensor([g], dtype=torch.float64))[0][0, 0, n, 0]) - val) > 1e-12 * max(1, val):
+                return True
+    except Exception:
+        return True
+    return False
+
+
+@pytest.mark.parametrize("kind", ["exclusive", "decay_off_by_one", "no_decay", "minus", "state_not_decayed",
+                                  "query_key_swapped", "heads_reversed"])
+def test_pins_reject_planted_mistakes(kind):
+    assert _pins_fail(_mutant(kind)), kind
+
+
+def test_pins_accept_the_oracle():
+    assert not _pins_fail(oracle.recurrent)
