@@ -1,0 +1,125 @@
+/*
+ * libretention — multi-scale retention on AMD Instinct MI355X (gfx950).
+ *
+ * The operator, per batch b and head h with decay gamma_h in [0, 1]:
+ *
+ *   Y_n = sum_{m <= n} gamma^(n-m) (Q_n . K_m) V_m  +  gamma^(n+1) Q_n S_in
+ *
+ * The first term is the retention definition of "Retentive Networks — Microsoft
+ * Propone l'Alternativa Architetturale ai Transformer" (aimpact.prandi.net),
+ * section "Il meccanismo: Multi-Scale Retention", which also gives the
+ * recurrent form S_n = gamma S_(n-1) + K_n^T V_n, Y_n = Q_n S_n, names the
+ * parallel and chunkwise forms as equivalent, and makes gamma a per-head
+ * hyperparameter.  The second term is the contribution of an initial state
+ * S_in (zero when none is passed).  No softmax, scale, clamp or denominator is
+ * applied (author answers to Q2 and Q3 on the paperhub.cn page "Retentive
+ * Network: A Successor to Transformer for Large Language Models"); the state
+ * has shape d_k x d_v (answer to Q1 on inference cost there).
+ *
+ * Conventions shared by every entry point
+ *   - Layouts (row-major, contiguous):
+ *       q, k : [B, H, T, dk]      v, y : [B, H, T, dv]
+ *       state: [B, H, dk, dv] fp32 (always fp32, whatever the input dtype)
+ *     decode step: q, k [B, H, dk]; v, y [B, H, dv]; state as above.
+ *   - q, k, v and y share one dtype (RET_F32 or RET_BF16); arithmetic and
+ *     accumulation are fp32; y is rounded to the dtype (round to nearest even).
+ *   - Every tensor pointer is a DEVICE pointer on the current HIP device,
+ *     owned by the caller; the library keeps no pointer after the call and
+ *     allocates no device memory.  Tensor pointers must be 16-byte aligned.
+ *   - gamma is a HOST array of H floats, read during the call only.
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously on it; no call synchronises the device.
+ *   - Validation happens before any HIP call.  On error nothing is enqueued,
+ *     no output is touched, and retention_last_error() describes the problem.
+ *   - Thread safety: calls from different host threads are independent;
+ *     the error text is thread-local.
+ */
+#ifndef LIBRETENTION_H_
+#define LIBRETENTION_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { RET_F32 = 0, RET_BF16 = 1 } ret_dtype;
+
+typedef enum {
+  RET_OK = 0,
+  RET_ERR_INVALID_ARG = 1, /* null required pointer, negative size, gamma not finite or outside [0,1] */
+  RET_ERR_UNSUPPORTED = 2, /* valid but outside what is built (see the limits below) */
+  RET_ERR_HIP = 3          /* a HIP launch failed; the text carries hipGetErrorString */
+} ret_status;
+
+/* Limits of this build: 1 <= dk <= 256, 1 <= dv <= 512, 1 <= C <= 128,
+ * B, H >= 1, T >= 0, B*H*T and every tensor's element count below 2^31. */
+#define RET_MAX_DK 256
+#define RET_MAX_DV 512
+#define RET_MAX_CHUNK 128
+
+/*
+ * Parallel form: Y = ((Q K^T) .* D) V + diag(gamma^(n+1)) Q S_in, with the causal
+ * decay mask D[n,m] = gamma^(n-m) for n >= m (D[n,n] = 1, also for gamma = 0)
+ * and 0 above the diagonal.  The aimpact page ("Il meccanismo") describes this
+ * form as computing the whole retention matrix at once, like attention; the
+ * baulab page "Retention Networks Explained" ("Methodology and Architecture")
+ * calls it the representation used for training.
+ *   state_in : nullable; fp32 [B,H,dk,dv].
+ *   y        : written, [B,H,T,dv] in dt.  Must not alias an input.
+ * O(T^2) work per head: meant for short sequences and as a cross-check.
+ */
+ret_status retention_parallel_fwd(const void* q, const void* k, const void* v, const float* gamma,
+                                  const float* state_in, void* y, int B, int H, int T, int dk, int dv,
+                                  ret_dtype dt, void* stream);
+
+/*
+ * Chunkwise form with chunk length C: the sequence is cut into chunks of C
+ * tokens (the last may be shorter); inside a chunk the parallel form runs, and
+ * a d_k x d_v state carries the past across chunks (aimpact page, "Il
+ * meccanismo").  For chunk i with rows j = 0..L-1 and carried state R_i:
+ *   Y_[i]   = ((Q_[i] K_[i]^T) .* D_L) V_[i] + diag(gamma^(j+1)) Q_[i] R_i
+ *   R_(i+1) = gamma^L R_i + (diag(gamma^(L-1-j)) K_[i])^T V_[i],  R_0 = S_in.
+ *   state_in  : nullable (zeros); fp32 [B,H,dk,dv].
+ *   state_out : nullable; receives R after the last token, fp32 [B,H,dk,dv].
+ *               May alias state_in exactly (in-place continuation).
+ *   y         : written, [B,H,T,dv] in dt; must not alias an input.
+ *   workspace : device scratch of at least retention_chunkwise_workspace_bytes()
+ *               bytes for the same arguments (may be NULL when that is 0).
+ * T = 0 is valid: y is untouched and state_out receives state_in (or zeros).
+ */
+ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, const float* gamma,
+                                   const float* state_in, float* state_out, void* y, int B, int H, int T,
+                                   int dk, int dv, int C, ret_dtype dt, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* Workspace size for retention_chunkwise_fwd with these arguments (0 when the
+ * chosen kernel needs none).  Returns (size_t)-1 for arguments the call would reject. */
+size_t retention_chunkwise_workspace_bytes(int B, int H, int T, int dk, int dv, int C, ret_dtype dt);
+
+/*
+ * One recurrent (decode) step, in place on the state: S <- gamma S + k^T v,
+ * then y = q S (the new state, so the current token is included).  This is the
+ * recurrent form of the aimpact page ("Il meccanismo"); the baulab page
+ * ("Methodology and Architecture") calls it the O(1)-per-token inference
+ * representation.
+ *   q, k  : [B,H,dk] in dt.   v : [B,H,dv] in dt.
+ *   state : in/out, fp32 [B,H,dk,dv]; required.
+ *   y     : written, [B,H,dv] in dt; must not alias the other arguments.
+ */
+ret_status retention_recurrent_step(const void* q, const void* k, const void* v, const float* gamma,
+                                    float* state, void* y, int B, int H, int dk, int dv, ret_dtype dt,
+                                    void* stream);
+
+/* Text of the last error on this host thread ("" after a successful call).
+ * Valid until the next libretention call on the same thread. */
+const char* retention_last_error(void);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int retention_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBRETENTION_H_ */

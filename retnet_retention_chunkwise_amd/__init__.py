@@ -1,0 +1,25 @@
+"""libretention: multi-scale retention on AMD Instinct MI355X (gfx950).
+
+The compute lives in hand-written HIP kernels behind a C ABI
+(include/libretention.h); this package is the thin Python binding:
+
+    chunkwise_fwd(q, k, v, gamma, C, state_in=None, state_out=True) -> (y, state_out)
+    parallel_fwd(q, k, v, gamma, state_in=None) -> y
+    recurrent_step(q, k, v, gamma, state) -> y          (state updated in place)
+
+Build the library with ``python -m retnet_retention_chunkwise_amd.build``.
+"""
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    MAX_CHUNK,
+    MAX_DK,
+    MAX_DV,
+    RetentionError,
+    chunkwise_fwd,
+    chunkwise_workspace_bytes,
+    last_error,
+    load,
+    parallel_fwd,
+    recurrent_step,
+    version,
+)

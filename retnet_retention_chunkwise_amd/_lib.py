@@ -1,0 +1,219 @@
+"""ctypes binding of libretention (argument marshalling only).
+
+Every computation runs in the HIP kernels of libretention.so; this module checks
+torch tensors (device, dtype, shape, contiguity), passes their device pointers
+and the current HIP stream through the C ABI, and turns a non-zero status into
+an exception.  There is no CPU fallback: without the built library every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple, Union
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libretention.so")
+
+RET_F32, RET_BF16 = 0, 1
+RET_OK, RET_ERR_INVALID_ARG, RET_ERR_UNSUPPORTED, RET_ERR_HIP = 0, 1, 2, 3
+MAX_DK, MAX_DV, MAX_CHUNK = 256, 512, 128
+
+# (name, restype, argtypes) of every symbol include/libretention.h declares
+_vp, _fp, _i, _sz = ctypes.c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.c_int, ctypes.c_size_t
+SIGNATURES = {
+    "retention_parallel_fwd": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
+    "retention_chunkwise_fwd": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "retention_chunkwise_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "retention_recurrent_step": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "retention_last_error": (ctypes.c_char_p, []),
+    "retention_version": (_i, []),
+}
+
+
+class RetentionError(RuntimeError):
+    """A libretention call returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[status {status}] {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libretention.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"libretention is not built ({p} missing); run `python -m retnet_retention_chunkwise_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().retention_last_error().decode()
+
+
+def version() -> int:
+    return int(load().retention_version())
+
+
+def _check(status: int):
+    if status != RET_OK:
+        raise RetentionError(status, last_error())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return RET_F32
+    if t.dtype == torch.bfloat16:
+        return RET_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (cuda/HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _gamma_array(gamma: Union[Sequence[float], torch.Tensor], H: int):
+    if isinstance(gamma, torch.Tensor):
+        vals = gamma.detach().to("cpu", torch.float32).reshape(-1).tolist()
+    else:
+        vals = [float(g) for g in gamma]
+    if len(vals) != H:
+        raise ValueError(f"gamma has {len(vals)} entries, expected H={H}")
+    return (ctypes.c_float * H)(*vals)
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _state_check(s: Optional[torch.Tensor], shape, device, name):
+    if s is None:
+        return
+    _dev(s, name)
+    if s.dtype != torch.float32 or tuple(s.shape) != tuple(shape) or s.device != device:
+        raise ValueError(f"{name} must be float32 {tuple(shape)} on {device}")
+
+
+def _qkv(q, k, v):
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("expected q, k [B,H,T,dk] and v [B,H,T,dv]")
+    if not (q.dtype == k.dtype == v.dtype) or not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must share dtype and device")
+    B, H, T, dk = q.shape
+    return B, H, T, dk, v.shape[-1], _dt(q)
+
+
+def chunkwise_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, C: int, dtype: torch.dtype) -> int:
+    dt = RET_BF16 if dtype == torch.bfloat16 else RET_F32
+    n = int(load().retention_chunkwise_workspace_bytes(B, H, T, dk, dv, C, dt))
+    if n == ctypes.c_size_t(-1).value:
+        raise RetentionError(RET_ERR_INVALID_ARG, "arguments rejected by retention_chunkwise_workspace_bytes")
+    return n
+
+
+def chunkwise_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma, C: int,
+                  state_in: Optional[torch.Tensor] = None, state_out: Union[torch.Tensor, bool, None] = True,
+                  y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise retention forward on the GPU (retention_chunkwise_fwd).
+
+    q, k [B,H,T,dk]; v [B,H,T,dv] (float32 or bfloat16, contiguous, on the GPU);
+    gamma: H decays in [0, 1]; C: chunk length.  state_in: optional fp32
+    [B,H,dk,dv].  state_out: a tensor to fill, True to allocate one, or
+    False/None for none (may be the same tensor as state_in).
+    Returns (y, state_out).
+    """
+    lib = load()
+    B, H, T, dk, dv, dt = _qkv(q, k, v)
+    sshape = (B, H, dk, dv)
+    _state_check(state_in, sshape, q.device, "state_in")
+    if state_out is True:
+        state_out = torch.empty(sshape, dtype=torch.float32, device=q.device)
+    elif state_out is False:
+        state_out = None
+    _state_check(state_out, sshape, q.device, "state_out")
+    if y is None:
+        y = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    else:
+        _dev(y, "y")
+        if y.shape != (B, H, T, dv) or y.dtype != q.dtype:
+            raise ValueError("y must match [B,H,T,dv] and the input dtype")
+    need = int(lib.retention_chunkwise_workspace_bytes(B, H, T, dk, dv, int(C), dt))
+    ws_bytes = 0
+    if need and need != ctypes.c_size_t(-1).value:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    elif workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.retention_chunkwise_fwd(_ptr(q), _ptr(k), _ptr(v), _gamma_array(gamma, H), _ptr(state_in),
+                                     _ptr(state_out), _ptr(y), B, H, T, dk, dv, int(C), dt, _ptr(workspace),
+                                     ws_bytes, _stream(q.device))
+    _check(st)
+    return y, state_out
+
+
+def parallel_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma,
+                 state_in: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Parallel-form retention forward on the GPU (retention_parallel_fwd)."""
+    lib = load()
+    B, H, T, dk, dv, dt = _qkv(q, k, v)
+    _state_check(state_in, (B, H, dk, dv), q.device, "state_in")
+    if y is None:
+        y = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    else:
+        _dev(y, "y")
+    st = lib.retention_parallel_fwd(_ptr(q), _ptr(k), _ptr(v), _gamma_array(gamma, H), _ptr(state_in), _ptr(y),
+                                    B, H, T, dk, dv, dt, _stream(q.device))
+    _check(st)
+    return y
+
+
+def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma, state: torch.Tensor,
+                   y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step on the GPU (retention_recurrent_step): state <- gamma*state + k^T v
+    in place, returns y = q state.  q, k [B,H,dk]; v [B,H,dv]; state fp32 [B,H,dk,dv]."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("expected q, k [B,H,dk] and v [B,H,dv]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dt(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    _state_check(state, (B, H, dk, dv), q.device, "state")
+    if y is None:
+        y = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    else:
+        _dev(y, "y")
+    st = lib.retention_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _gamma_array(gamma, H), _ptr(state), _ptr(y),
+                                      B, H, dk, dv, dt, _stream(q.device))
+    _check(st)
+    return y

@@ -1,0 +1,191 @@
+// C-ABI layer of libretention: argument validation, per-head decay tables,
+// kernel choice and launch.  Every check happens before the first HIP call, so
+// a rejected call enqueues nothing and touches no output.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+#include "libretention.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ret_status fail(ret_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ret_status ok() {
+  g_last_error.clear();
+  return RET_OK;
+}
+
+ret_status hip_fail(const char* fn, hipError_t e) {
+  return fail(RET_ERR_HIP, "%s: HIP error %d (%s)", fn, static_cast<int>(e), hipGetErrorString(e));
+}
+
+constexpr long long kMaxElems = (1LL << 31) - 1;
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Shared checks of sizes, dtype and gamma.
+ret_status check_common(const char* fn, int B, int H, int T, int dk, int dv, ret_dtype dt, const float* gamma) {
+  if (B < 1 || H < 1) return fail(RET_ERR_INVALID_ARG, "%s: B=%d and H=%d must be >= 1", fn, B, H);
+  if (T < 0) return fail(RET_ERR_INVALID_ARG, "%s: T=%d must be >= 0", fn, T);
+  if (dk < 1 || dv < 1) return fail(RET_ERR_INVALID_ARG, "%s: dk=%d and dv=%d must be >= 1", fn, dk, dv);
+  if (dt != RET_F32 && dt != RET_BF16) return fail(RET_ERR_UNSUPPORTED, "%s: dtype %d is not RET_F32 or RET_BF16", fn, static_cast<int>(dt));
+  if (gamma == nullptr) return fail(RET_ERR_INVALID_ARG, "%s: gamma (host array of H floats) is null", fn);
+  for (int h = 0; h < H; ++h) {
+    const float g = gamma[h];
+    if (!std::isfinite(g) || g < 0.0f || g > 1.0f)
+      return fail(RET_ERR_INVALID_ARG, "%s: gamma[%d] = %g is not a decay in [0, 1]", fn, h, static_cast<double>(g));
+  }
+  if (dk > RET_MAX_DK || dv > RET_MAX_DV)
+    return fail(RET_ERR_UNSUPPORTED, "%s: dk=%d, dv=%d exceed the built limits (dk <= %d, dv <= %d)", fn, dk, dv,
+                RET_MAX_DK, RET_MAX_DV);
+  const long long bh = static_cast<long long>(B) * H;
+  if (bh * T * dk > kMaxElems || bh * T * dv > kMaxElems || bh * dk * dv > kMaxElems)
+    return fail(RET_ERR_UNSUPPORTED, "%s: a tensor has 2^31 or more elements", fn);
+  return RET_OK;
+}
+
+size_t dsize(ret_dtype dt) { return dt == RET_F32 ? 4 : 2; }
+
+template <typename F>
+ret_status for_head_groups(const char* fn, int H, const float* gamma, F&& launch) {
+  for (int h0 = 0; h0 < H; h0 += ret::kHeadsPerLaunch) {
+    ret::HeadGroup g{h0, H - h0 < ret::kHeadsPerLaunch ? H - h0 : ret::kHeadsPerLaunch, gamma + h0};
+    const hipError_t e = launch(g);
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
+  return ok();
+}
+
+}  // namespace
+
+namespace ret {
+HeadDecay make_head_decay(const HeadGroup& g) {
+  HeadDecay hd;
+  for (int i = 0; i < kHeadsPerLaunch; ++i) {
+    const double gm = i < g.nh ? static_cast<double>(g.gamma[i]) : 1.0;
+    hd.log2g[i] = gm > 0.0 ? static_cast<float>(std::log2(gm)) : -INFINITY;
+  }
+  return hd;
+}
+}  // namespace ret
+
+extern "C" {
+
+const char* retention_last_error(void) { return g_last_error.c_str(); }
+
+int retention_version(void) { return 100; }
+
+ret_status retention_recurrent_step(const void* q, const void* k, const void* v, const float* gamma, float* state,
+                                    void* y, int B, int H, int dk, int dv, ret_dtype dt, void* stream) {
+  const char* fn = "retention_recurrent_step";
+  ret_status st = check_common(fn, B, H, 1, dk, dv, dt, gamma);
+  if (st != RET_OK) return st;
+  if (!q || !k || !v || !state || !y) return fail(RET_ERR_INVALID_ARG, "%s: q, k, v, state and y are required", fn);
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(state) || misaligned(y))
+    return fail(RET_ERR_UNSUPPORTED, "%s: tensor pointers must be 16-byte aligned", fn);
+  const size_t es = dsize(dt);
+  const size_t bh = static_cast<size_t>(B) * H;
+  const size_t ny = bh * dv * es;
+  if (overlap(y, ny, q, bh * dk * es) || overlap(y, ny, k, bh * dk * es) || overlap(y, ny, v, ny) ||
+      overlap(y, ny, state, bh * dk * dv * 4))
+    return fail(RET_ERR_INVALID_ARG, "%s: y overlaps an input or the state", fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return for_head_groups(fn, H, gamma, [&](const ret::HeadGroup& g) {
+    return ret::launch_recurrent_step(q, k, v, state, y, B, H, dk, dv, static_cast<int>(dt), g, s);
+  });
+}
+
+ret_status retention_parallel_fwd(const void* q, const void* k, const void* v, const float* gamma,
+                                  const float* state_in, void* y, int B, int H, int T, int dk, int dv, ret_dtype dt,
+                                  void* stream) {
+  const char* fn = "retention_parallel_fwd";
+  ret_status st = check_common(fn, B, H, T, dk, dv, dt, gamma);
+  if (st != RET_OK) return st;
+  if (T > 0 && (!q || !k || !v || !y)) return fail(RET_ERR_INVALID_ARG, "%s: q, k, v and y are required", fn);
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(y) || misaligned(state_in))
+    return fail(RET_ERR_UNSUPPORTED, "%s: tensor pointers must be 16-byte aligned", fn);
+  const size_t es = dsize(dt);
+  const size_t bht = static_cast<size_t>(B) * H * T;
+  const size_t ny = bht * dv * es;
+  if (overlap(y, ny, q, bht * dk * es) || overlap(y, ny, k, bht * dk * es) || overlap(y, ny, v, ny) ||
+      overlap(y, ny, state_in, static_cast<size_t>(B) * H * dk * dv * 4))
+    return fail(RET_ERR_INVALID_ARG, "%s: y overlaps an input", fn);
+  if (T == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return for_head_groups(fn, H, gamma, [&](const ret::HeadGroup& g) {
+    return ret::launch_parallel_fwd(q, k, v, state_in, y, B, H, T, dk, dv, static_cast<int>(dt), g, s);
+  });
+}
+
+size_t retention_chunkwise_workspace_bytes(int B, int H, int T, int dk, int dv, int C, ret_dtype dt) {
+  if (B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1 || C < 1) return static_cast<size_t>(-1);
+  if (dk > RET_MAX_DK || dv > RET_MAX_DV || C > RET_MAX_CHUNK) return static_cast<size_t>(-1);
+  if (dt != RET_F32 && dt != RET_BF16) return static_cast<size_t>(-1);
+  return 0;
+}
+
+ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, const float* gamma,
+                                   const float* state_in, float* state_out, void* y, int B, int H, int T, int dk,
+                                   int dv, int C, ret_dtype dt, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  const char* fn = "retention_chunkwise_fwd";
+  ret_status st = check_common(fn, B, H, T, dk, dv, dt, gamma);
+  if (st != RET_OK) return st;
+  if (C < 1) return fail(RET_ERR_INVALID_ARG, "%s: chunk length C=%d must be >= 1", fn, C);
+  if (C > RET_MAX_CHUNK) return fail(RET_ERR_UNSUPPORTED, "%s: chunk length C=%d exceeds %d", fn, C, RET_MAX_CHUNK);
+  if (T > 0 && (!q || !k || !v || !y)) return fail(RET_ERR_INVALID_ARG, "%s: q, k, v and y are required", fn);
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(y) || misaligned(state_in) ||
+      misaligned(state_out) || misaligned(workspace))
+    return fail(RET_ERR_UNSUPPORTED, "%s: tensor pointers must be 16-byte aligned", fn);
+  const size_t need = retention_chunkwise_workspace_bytes(B, H, T, dk, dv, C, dt);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(RET_ERR_INVALID_ARG, "%s: workspace of %zu bytes required, %zu given", fn, need, workspace_bytes);
+  const size_t es = dsize(dt);
+  const size_t bht = static_cast<size_t>(B) * H * T;
+  const size_t ny = bht * dv * es;
+  const size_t ns = static_cast<size_t>(B) * H * dk * dv * 4;
+  if (overlap(y, ny, q, bht * dk * es) || overlap(y, ny, k, bht * dk * es) || overlap(y, ny, v, ny) ||
+      overlap(y, ny, state_in, ns) || overlap(y, ny, state_out, ns))
+    return fail(RET_ERR_INVALID_ARG, "%s: y overlaps an input or a state buffer", fn);
+  if (state_in != state_out && overlap(state_in, ns, state_out, ns))
+    return fail(RET_ERR_INVALID_ARG, "%s: state_in and state_out overlap without being the same buffer", fn);
+  if (state_out != nullptr && (overlap(state_out, ns, q, bht * dk * es) || overlap(state_out, ns, k, bht * dk * es) ||
+                               overlap(state_out, ns, v, ny)))
+    return fail(RET_ERR_INVALID_ARG, "%s: state_out overlaps an input", fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    if (state_out == nullptr || state_out == state_in) return ok();
+    const hipError_t e = ret::launch_state_copy(state_in, state_out, ns / 4, s);
+    return e == hipSuccess ? ok() : hip_fail(fn, e);
+  }
+  const bool mfma = ret::chunkwise_mfma_supports(T, dk, dv, C, static_cast<int>(dt));
+  return for_head_groups(fn, H, gamma, [&](const ret::HeadGroup& g) {
+    if (mfma) return ret::launch_chunkwise_mfma(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, g, s);
+    return ret::launch_chunkwise_generic(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, static_cast<int>(dt),
+                                         g, s);
+  });
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the kernels.
+// Arguments are validated by the caller; these functions only enqueue work.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+
+namespace ret {
+
+// Per-launch head decay table, passed by value as a kernel argument.  A launch
+// covers at most kHeadsPerLaunch heads; the host splits larger H into groups.
+constexpr int kHeadsPerLaunch = 128;
+struct HeadDecay {
+  float log2g[kHeadsPerLaunch];  // log2(gamma_h); -inf for gamma_h = 0
+};
+
+struct HeadGroup {
+  int h0;              // first head of this launch
+  int nh;              // number of heads in this launch (<= 128)
+  const float* gamma;  // host, gamma of head h0 + i at gamma[i]
+};
+
+// log2(gamma) of the group's heads, computed in double on the host.
+HeadDecay make_head_decay(const HeadGroup& g);
+
+// dt: 0 = fp32, 1 = bf16 (raw bits).
+hipError_t launch_recurrent_step(const void* q, const void* k, const void* v, float* state, void* y, int B,
+                                 int H, int dk, int dv, int dt, const HeadGroup& g, hipStream_t s);
+
+hipError_t launch_parallel_fwd(const void* q, const void* k, const void* v, const float* state_in, void* y,
+                               int B, int H, int T, int dk, int dv, int dt, const HeadGroup& g, hipStream_t s);
+
+// Generic VALU chunkwise kernel (any supported shape, fp32 or bf16 inputs).
+hipError_t launch_chunkwise_generic(const void* q, const void* k, const void* v, const float* state_in,
+                                    float* state_out, void* y, int B, int H, int T, int dk, int dv, int C,
+                                    int dt, const HeadGroup& g, hipStream_t s);
+
+// bf16 MFMA chunkwise kernel; chunkwise_mfma_supports() says whether it takes a shape.
+bool chunkwise_mfma_supports(int T, int dk, int dv, int C, int dt);
+hipError_t launch_chunkwise_mfma(const void* q, const void* k, const void* v, const float* state_in,
+                                 float* state_out, void* y, int B, int H, int T, int dk, int dv, int C,
+                                 const HeadGroup& g, hipStream_t s);
+
+// Copies state_in (or zeros when null) into state_out: the T = 0 case.
+hipError_t launch_state_copy(const float* state_in, float* state_out, size_t n, hipStream_t s);
+
+}  // namespace ret

@@ -27,3 +27,12 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_sessionstart(session):
+    # The ABI tests load the built library; build it once if it is missing.
+    lib = os.path.join(ROOT, "retnet_retention_chunkwise_amd", "libretention.so")
+    if not os.path.exists(lib):
+        from retnet_retention_chunkwise_amd import build
+
+        build.build()

@@ -1,0 +1,122 @@
+"""C-ABI checks that run without a GPU.
+
+The library must load, export every function include/libretention.h declares,
+and reject invalid arguments before making any HIP call (so these calls are
+safe on a machine without a device: nothing is launched).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from retnet_retention_chunkwise_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libretention.h")
+
+INVALID, UNSUPPORTED = _lib.RET_ERR_INVALID_ARG, _lib.RET_ERR_UNSUPPORTED
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced: every call below fails validation first
+FAKE_MIS = ctypes.c_void_p(0x10004)    # not 16-byte aligned
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(retention_\w+)\s*\(", text, flags=re.M)))
+
+
+def gam(*vals):
+    return (ctypes.c_float * len(vals))(*vals)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == set(_lib.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.retention_version() == 100
+
+
+def chunk(lib, q=FAKE, k=FAKE, v=FAKE, g=None, sin=None, sout=None, y=ctypes.c_void_p(0x20000), B=1, H=2, T=8,
+          dk=16, dv=16, C=4, dt=0, ws=None, wsb=0):
+    g = gam(0.5, 0.9) if g is None else g
+    return lib.retention_chunkwise_fwd(q, k, v, g, sin, sout, y, B, H, T, dk, dv, C, dt, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(B=0), INVALID, "B=0"),
+    (dict(H=0), INVALID, "H=0"),
+    (dict(T=-1), INVALID, "T=-1"),
+    (dict(dk=0), INVALID, "dk=0"),
+    (dict(C=0), INVALID, "chunk length"),
+    (dict(C=129), UNSUPPORTED, "exceeds"),
+    (dict(dk=257), UNSUPPORTED, "exceed"),
+    (dict(dv=513), UNSUPPORTED, "exceed"),
+    (dict(dt=7), UNSUPPORTED, "dtype"),
+    (dict(q=None), INVALID, "required"),
+    (dict(y=None), INVALID, "required"),
+    (dict(q=FAKE_MIS), UNSUPPORTED, "aligned"),
+    (dict(g=(ctypes.c_float * 2)(0.5, 1.5)), INVALID, "gamma[1]"),
+    (dict(g=(ctypes.c_float * 2)(-0.1, 0.5)), INVALID, "gamma[0]"),
+    (dict(g=(ctypes.c_float * 2)(float("nan"), 0.5)), INVALID, "gamma[0]"),
+    (dict(g=(ctypes.c_float * 2)(0.5, float("inf"))), INVALID, "gamma[1]"),
+    (dict(y=FAKE), INVALID, "overlaps"),
+    (dict(sin=ctypes.c_void_p(0x40000), sout=ctypes.c_void_p(0x40010)), INVALID, "overlap"),
+    (dict(B=1 << 16, H=1 << 10, T=1 << 10, g=(ctypes.c_float * 1024)(*([0.5] * 1024))), UNSUPPORTED, "2^31"),
+])
+def test_chunkwise_rejects(lib, kw, status, needle):
+    assert chunk(lib, **kw) == status
+    assert needle in _lib.last_error(), _lib.last_error()
+
+
+def test_null_gamma_rejected(lib):
+    st = lib.retention_chunkwise_fwd(FAKE, FAKE, FAKE, None, None, None, FAKE, 1, 1, 4, 4, 4, 4, 0, None, 0, None)
+    assert st == INVALID and "gamma" in _lib.last_error()
+
+
+def test_recurrent_step_rejects(lib):
+    g = gam(0.5)
+    st = lib.retention_recurrent_step(FAKE, FAKE, FAKE, g, None, ctypes.c_void_p(0x90000), 1, 1, 4, 4, 0, None)
+    assert st == INVALID and "required" in _lib.last_error()
+    st = lib.retention_recurrent_step(FAKE, FAKE, FAKE, gam(2.0), ctypes.c_void_p(0x50000),
+                                      ctypes.c_void_p(0x90000), 1, 1, 4, 4, 0, None)
+    assert st == INVALID and "gamma[0]" in _lib.last_error()
+    st = lib.retention_recurrent_step(FAKE, FAKE, FAKE, g, ctypes.c_void_p(0x50000), ctypes.c_void_p(0x50000),
+                                      1, 1, 4, 4, 0, None)
+    assert st == INVALID and "overlaps" in _lib.last_error()
+
+
+def test_parallel_rejects(lib):
+    st = lib.retention_parallel_fwd(FAKE, FAKE, FAKE, gam(0.5), None, None, 1, 1, 4, 4, 4, 0, None)
+    assert st == INVALID
+    st = lib.retention_parallel_fwd(FAKE, FAKE, FAKE, gam(0.5), None, ctypes.c_void_p(0x90000), 1, 1, 4, 300, 4, 0,
+                                    None)
+    assert st == UNSUPPORTED
+
+
+def test_workspace_query(lib):
+    assert lib.retention_chunkwise_workspace_bytes(1, 2, 64, 16, 16, 16, 0) == 0
+    bad = ctypes.c_size_t(-1).value
+    assert lib.retention_chunkwise_workspace_bytes(0, 2, 64, 16, 16, 16, 0) == bad
+    assert lib.retention_chunkwise_workspace_bytes(1, 2, 64, 16, 16, 0, 0) == bad
+    assert lib.retention_chunkwise_workspace_bytes(1, 2, 64, 16, 16, 16, 5) == bad
+
+
+def test_error_text_is_cleared_by_success_path_query(lib):
+    chunk(lib, B=0)
+    assert _lib.last_error() != ""
+
+
+def test_python_wrapper_refuses_cpu_tensors():
+    import torch
+
+    q = torch.zeros(1, 1, 4, 4)
+    with pytest.raises(ValueError):
+        _lib.chunkwise_fwd(q, q, q, [0.5], 4)
+    with pytest.raises(ValueError):
+        _lib.recurrent_step(q[0], q[0], q[0], [0.5], torch.zeros(1, 1, 4, 4))

@@ -1,0 +1,225 @@
+"""GPU parity of libretention against the fp64 CPU oracle (MI355X).
+
+Every test calls the HIP kernels through the C ABI (via the ctypes binding)
+on seeded synthetic inputs and compares element by element with the oracle on
+the same input values: rel-L2 <= 1e-4 for fp32 inputs and <= 2e-2 for bf16
+inputs, on y and on the carried state.  Full-size workloads are checked on
+sampled heads that the oracle computes.
+"""
+import pytest
+import torch
+
+import oracle
+import retnet_retention_chunkwise_amd as ret
+from retnet_retention_chunkwise_amd.workloads import WORKLOADS, make_decode_inputs, make_inputs
+from helpers import rel_l2, say, tol
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def to_dev(*ts):
+    return [None if t is None else t.to(DEV) for t in ts]
+
+
+def check(name, got, want, bound):
+    r = rel_l2(got, want)
+    say(f"{name}: rel-L2 {r:.3e} (bound {bound:.0e})")
+    assert torch.isfinite(got.float()).all(), name
+    assert r <= bound, (name, r)
+
+
+def gammas_for(H, lo=0.3):
+    return [lo + (1.0 - lo) * h / max(1, H - 1) for h in range(H)]
+
+
+# ------------------------------------------------------------------ tiny
+def test_tiny_all_three_forms():
+    wl = WORKLOADS["tiny"]
+    say("tiny workload: parallel, chunkwise C=16, 64 recurrent steps (fp32)")
+    q, k, v = make_inputs(wl.B, wl.H, wl.T, wl.dk, wl.dv, wl.dtype, seed=0)
+    g = list(wl.gammas)
+    y_ref, s_ref = oracle.recurrent(q, k, v, torch.tensor(g, dtype=torch.float64))
+    qd, kd, vd = to_dev(q, k, v)
+    check("tiny parallel", ret.parallel_fwd(qd, kd, vd, g), y_ref, 1e-4)
+    y, s = ret.chunkwise_fwd(qd, kd, vd, g, wl.C)
+    check("tiny chunkwise y", y, y_ref, 1e-4)
+    check("tiny chunkwise state", s, s_ref, 1e-4)
+    state = torch.zeros(wl.B, wl.H, wl.dk, wl.dv, device=DEV)
+    ys = []
+    for n in range(wl.T):
+        ys.append(ret.recurrent_step(qd[:, :, n].contiguous(), kd[:, :, n].contiguous(), vd[:, :, n].contiguous(), g,
+                                     state))
+    check("tiny recurrent y", torch.stack(ys, dim=2), y_ref, 1e-4)
+    check("tiny recurrent state", state, s_ref, 1e-4)
+
+
+# ------------------------------------------------------- chunkwise edge cases
+CHUNK_CASES = [
+    # B, H, T, dk, dv, C, dtype, with_state, gammas
+    (1, 3, 100, 16, 16, 16, "f32", True, [0.0, 0.5, 1.0]),
+    (2, 2, 257, 64, 96, 32, "f32", True, [0.9, 0.99]),
+    (1, 1, 1, 8, 8, 16, "f32", False, [0.7]),
+    (1, 2, 50, 7, 5, 8, "f32", True, [0.6, 0.95]),
+    (1, 2, 300, 16, 16, 1, "f32", False, [0.8, 0.3]),
+    (1, 2, 300, 32, 48, 128, "f32", True, [0.999, 0.5]),
+    (1, 130, 20, 4, 4, 4, "f32", True, None),
+    (1, 2, 300, 64, 128, 64, "bf16", True, [0.97, 0.6]),
+    (2, 2, 200, 48, 80, 32, "bf16", False, [0.0, 1.0]),
+    (1, 2, 129, 256, 512, 128, "bf16", True, [0.99, 0.9]),
+    (2, 3, 385, 128, 192, 64, "bf16", True, [0.999, 0.95, 0.5]),
+    (1, 2, 70, 256, 64, 16, "bf16", True, [0.9, 0.97]),
+    (1, 1, 33, 32, 64, 32, "bf16", False, [1.0]),
+]
+
+
+@pytest.mark.parametrize("B,H,T,dk,dv,C,dt,with_state,gs", CHUNK_CASES)
+def test_chunkwise_vs_oracle(B, H, T, dk, dv, C, dt, with_state, gs):
+    say(f"chunkwise B{B} H{H} T{T} dk{dk} dv{dv} C{C} {dt} state={with_state}")
+    gs = gs if gs is not None else gammas_for(H)
+    q, k, v, s0 = make_inputs(B, H, T, dk, dv, dt, seed=1, with_state=True)
+    if not with_state:
+        s0 = None
+    y_ref, s_ref = oracle.recurrent(q, k, v, torch.tensor(gs, dtype=torch.float32), s0)
+    qd, kd, vd, sd = to_dev(q, k, v, s0)
+    y, s = ret.chunkwise_fwd(qd, kd, vd, gs, C, state_in=sd)
+    torch.cuda.synchronize()
+    bound = tol(q.dtype)
+    check("y", y, y_ref, bound)
+    check("state_out", s, s_ref, bound)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_parallel_vs_oracle(dt):
+    B, H, T, dk, dv = 2, 3, 150, 32, 64
+    say(f"parallel B{B} H{H} T{T} dk{dk} dv{dv} {dt}")
+    gs = [0.0, 0.8, 1.0]
+    q, k, v, s0 = make_inputs(B, H, T, dk, dv, dt, seed=2, with_state=True)
+    y_ref = oracle.parallel(q, k, v, torch.tensor(gs, dtype=torch.float32), s0)
+    qd, kd, vd, sd = to_dev(q, k, v, s0)
+    check("parallel y", ret.parallel_fwd(qd, kd, vd, gs, state_in=sd), y_ref, tol(q.dtype))
+
+
+@pytest.mark.parametrize("dt,dv", [("f32", 64), ("bf16", 512), ("f32", 30), ("bf16", 6)])
+def test_recurrent_steps_vs_oracle(dt, dv):
+    B, H, dk, steps = 3, 4, 64, 12
+    say(f"recurrent steps B{B} H{H} dk{dk} dv{dv} {dt}")
+    gs = [0.0, 0.5, 0.9, 1.0]
+    q, k, v, s0 = make_decode_inputs(B, H, dk, dv, steps, dt, seed=3)
+    state = s0.to(DEV)
+    S = s0
+    ys, yr = [], []
+    for n in range(steps):
+        ys.append(ret.recurrent_step(q[n].to(DEV), k[n].to(DEV), v[n].to(DEV), gs, state).cpu())
+        y_n, S = oracle.recurrent_step(q[n], k[n], v[n], torch.tensor(gs, dtype=torch.float32), S)
+        yr.append(y_n)
+    check("decode y", torch.stack(ys), torch.stack(yr), tol(q.dtype))
+    check("decode state", state, S, tol(q.dtype))
+
+
+# ------------------------------------------------------- state semantics
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_split_sequence_with_state_handoff(dt):
+    B, H, T, dk, dv, C = 1, 2, 260, 64, 128, 32
+    say(f"state handoff {dt}")
+    gs = [0.95, 0.7]
+    q, k, v, s0 = make_inputs(B, H, T, dk, dv, dt, seed=4, with_state=True)
+    qd, kd, vd, sd = to_dev(q, k, v, s0)
+    y_all, s_all = ret.chunkwise_fwd(qd, kd, vd, gs, C, state_in=sd)
+    t = 100  # not a multiple of C
+    st = sd.clone()
+    y1, _ = ret.chunkwise_fwd(qd[:, :, :t].contiguous(), kd[:, :, :t].contiguous(), vd[:, :, :t].contiguous(), gs, C,
+                              state_in=st, state_out=st)       # in place: state_out aliases state_in
+    y2, _ = ret.chunkwise_fwd(qd[:, :, t:].contiguous(), kd[:, :, t:].contiguous(), vd[:, :, t:].contiguous(), gs, C,
+                              state_in=st, state_out=st)
+    y_ref, s_ref = oracle.recurrent(q, k, v, torch.tensor(gs, dtype=torch.float32), s0)
+    check("split y", torch.cat([y1, y2], dim=2), y_ref, tol(q.dtype))
+    check("split state", st, s_ref, tol(q.dtype))
+    check("split vs one call", torch.cat([y1, y2], dim=2), y_all, tol(q.dtype))
+
+
+def test_empty_sequence_copies_state():
+    say("T = 0")
+    B, H, dk, dv = 1, 2, 16, 32
+    e = torch.empty(B, H, 0, dk, device=DEV)
+    ev = torch.empty(B, H, 0, dv, device=DEV)
+    s_in = torch.randn(B, H, dk, dv, device=DEV)
+    y, s = ret.chunkwise_fwd(e, e, ev, [0.5, 0.5], 16, state_in=s_in)
+    assert y.shape == (B, H, 0, dv)
+    assert torch.equal(s, s_in)
+    _, s0 = ret.chunkwise_fwd(e, e, ev, [0.5, 0.5], 16)
+    assert torch.count_nonzero(s0) == 0
+
+
+def test_chunk_length_independence_on_gpu():
+    B, H, T, dk, dv = 1, 2, 257, 128, 128
+    say("chunk length independence, bf16")
+    gs = [0.98, 0.8]
+    q, k, v = to_dev(*make_inputs(B, H, T, dk, dv, "bf16", seed=5))
+    y_ref, s_ref = oracle.recurrent(q.cpu(), k.cpu(), v.cpu(), torch.tensor(gs, dtype=torch.float32))
+    for C in (8, 16, 32, 64, 100, 128):
+        y, s = ret.chunkwise_fwd(q, k, v, gs, C)
+        check(f"C={C} y", y, y_ref, 2e-2)
+        check(f"C={C} state", s, s_ref, 2e-2)
+
+
+def test_deterministic_reruns():
+    say("bitwise determinism of reruns")
+    B, H, T, dk, dv, C = 2, 4, 512, 256, 512, 64
+    q, k, v = to_dev(*make_inputs(B, H, T, dk, dv, "bf16", seed=6))
+    gs = gammas_for(H, 0.9)
+    y1, s1 = ret.chunkwise_fwd(q, k, v, gs, C)
+    y2, s2 = ret.chunkwise_fwd(q, k, v, gs, C)
+    assert torch.equal(y1, y2) and torch.equal(s1, s2)
+
+
+# ------------------------------------------------------- full-size workloads
+def sampled_heads(B, H):
+    return sorted({(0, 0), (B // 2, H // 2), (B - 1, H - 1)})
+
+
+@pytest.mark.parametrize("key", ["layer1p3b", "layer6p7b", "long64k"])
+def test_full_size_workload_sampled_heads(key):
+    wl = WORKLOADS[key]
+    say(f"full workload {key}: {wl.description}")
+    q, k, v = make_inputs(wl.B, wl.H, wl.T, wl.dk, wl.dv, wl.dtype, seed=0)
+    qd, kd, vd = to_dev(q, k, v)
+    y, s = ret.chunkwise_fwd(qd, kd, vd, list(wl.gammas), wl.C)
+    torch.cuda.synchronize()
+    say(f"{key}: kernel done, checking sampled heads against the oracle")
+    assert torch.isfinite(y.float()).all()
+    for b, h in sampled_heads(wl.B, wl.H):
+        g = torch.tensor([wl.gammas[h]], dtype=torch.float32)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        y_ref, s_ref = oracle.chunkwise(q[sl], k[sl], v[sl], g, wl.C)
+        check(f"{key} y[b={b},h={h}]", y[sl].cpu(), y_ref, 2e-2)
+        check(f"{key} state[b={b},h={h}]", s[sl].cpu(), s_ref, 2e-2)
+
+
+def test_full_size_decode_1000_steps_sampled_heads():
+    wl = WORKLOADS["decode"]
+    say(f"full decode: {wl.description}")
+    q, k, v, s0 = make_decode_inputs(wl.B, wl.H, wl.dk, wl.dv, wl.steps, wl.dtype, seed=0)
+    qd, kd, vd = to_dev(q, k, v)
+    state = s0.to(DEV)
+    ys = torch.empty(wl.steps, wl.B, wl.H, wl.dv, dtype=qd.dtype, device=DEV)
+    g = list(wl.gammas)
+    for n in range(wl.steps):
+        ret.recurrent_step(qd[n], kd[n], vd[n], g, state, y=ys[n])
+    torch.cuda.synchronize()
+    say("decode: 1000 steps done, checking sampled heads against the oracle")
+    num = den = 0.0
+    for b, h in sampled_heads(wl.B, wl.H):
+        S = s0[b:b + 1, h:h + 1]
+        gh = torch.tensor([wl.gammas[h]], dtype=torch.float32)
+        got = ys[:, b, h].cpu().double()
+        for n in range(wl.steps):
+            y_n, S = oracle.recurrent_step(q[n, b:b + 1, h:h + 1], k[n, b:b + 1, h:h + 1], v[n, b:b + 1, h:h + 1],
+                                           gh, S)
+            num += float((got[n] - y_n[0, 0]).pow(2).sum())
+            den += float(y_n.pow(2).sum())
+        check(f"decode state[b={b},h={h}]", state[b, h].cpu(), S[0, 0], 2e-2)
+    r = (num / den) ** 0.5
+    say(f"decode y over sampled heads: rel-L2 {r:.3e}")
+    assert r <= 2e-2
