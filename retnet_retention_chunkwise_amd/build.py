@@ -33,8 +33,11 @@ SOURCES = [
 ARCH = "gfx950"
 # Packed-fp32 VALU instructions are kept off: hipcc would otherwise form them
 # from ordinary float code.
+# MFMA results go to arch VGPRs (not AGPRs), which avoids AGPR<->VGPR copies
+# around the VALU work on accumulators (decay masks, state scaling).
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-          "-packed-fp32-ops", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
+          "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form=true", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall",
+          "-Wno-unused-function"]
 
 
 def _hipcc() -> str:

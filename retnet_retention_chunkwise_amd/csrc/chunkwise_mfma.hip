@@ -42,7 +42,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kThreads = 256;
 constexpr int kTN = 64;  // value columns per workgroup
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -63,26 +62,47 @@ __device__ __forceinline__ bf16x8 join(s16x4 lo, s16x4 hi) {
 
 __device__ __forceinline__ bf16x8 lds_read16(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-template <int CT, int DK>
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0,
+// stores past the end are dropped.  0x00020000 is the gfx9 data-format word.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+}
+__device__ __forceinline__ void buffer_store2(rsrc_t r, uint32_t off, uint16_t x) {
+  __builtin_amdgcn_raw_buffer_store_b16(x, r, static_cast<int>(off), 0, 0);
+}
+
+template <int CT, int DK, int NW>
 struct Cfg {
+  static constexpr int kThreads = 64 * NW;
   static constexpr int KLD = DK + 8;           // K row stride in LDS (elements)
   static constexpr int VLD = kTN + 8;          // V / zeta*V row stride
   static constexpr int RLD = DK + 8;           // R^T row stride
-  static constexpr int NQ = CT / 64;           // query blocks per wave
-  static constexpr int RM = DK / 64;           // 16-row state blocks per wave
+  static constexpr int NQ = CT / (16 * NW);    // query blocks per wave
+  static constexpr int RM = DK / (16 * NW);    // 16-row state blocks per wave
   static constexpr int KS = DK / 32;           // k-steps over d_k
   static constexpr int KPT = CT * DK / 8 / kThreads;   // 16-byte K pieces per thread
   static constexpr int VPT = CT * kTN / 8 / kThreads;  // 16-byte V pieces per thread
+  static_assert(NQ >= 1 && NQ <= 2 && RM >= 1, "unsupported wave split");
   static_assert(KPT >= 1 && VPT >= 1, "tile too small for the staging split");
 };
 
-template <int CT, int DK>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1))) void
+template <int CT, int DK, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(NW / 4, NW / 4))) void
 chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                       const uint16_t* __restrict__ v, const float* state_in, float* state_out,
                       uint16_t* __restrict__ y, HeadDecay gam, int H, int h0, int nh, int Tn, int dv, int C,
                       int ntiles) {
-  using F = Cfg<CT, DK>;
+  using F = Cfg<CT, DK, NW>;
+  constexpr int kThreads = F::kThreads;
+  constexpr int NSP = CT / 32;  // key steps of 32 keys per chunk tile
+  constexpr int NKB = CT / 16;  // 16-row blocks per chunk tile
   __shared__ __attribute__((aligned(16))) uint16_t Ks[CT * F::KLD];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[CT * F::VLD];
   __shared__ __attribute__((aligned(16))) uint16_t Vz[CT * F::VLD];
@@ -90,7 +110,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar) by construction
   const int c16 = lane & 15;
   const int g = lane >> 4;
 
@@ -113,15 +133,34 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const uint16_t* vh = v + head * Tn * dv + col0;
   uint16_t* yh = y + head * Tn * dv + col0;
   const long sbase = head * static_cast<long>(DK) * dv + col0;
+  const uint32_t vrow = static_cast<uint32_t>(dv) * 2u;  // bytes per V / Y row
 
+  // Query blocks of this wave.  Waves w and w+4 share a SIMD; the pairings
+  // below give every SIMD query blocks {s, 7-s} of a 128-token chunk, which
+  // balances the causal triangle.
   int qblk[F::NQ];
   if constexpr (F::NQ == 2) {
     qblk[0] = w;
     qblk[1] = 7 - w;
+  } else if constexpr (NW == 8) {
+    qblk[0] = w < 4 ? w : 11 - w;
   } else {
     qblk[0] = w;
   }
-  const int dbase = w * (DK / 4);
+  const int dbase = w * (DK / NW);
+
+  // ---- decay factors that do not depend on the chunk (positions are chunk-relative)
+  // off-diagonal key block kb < qb: gamma^(j-t) = gamma^(16(qb-kb) + c16 - 4g - 3) * cst[t & 3]
+  //   (first exponent >= 1), cst[e] = gamma^(3-e);
+  // diagonal key block kb == qb: Ddg[e] = gamma^(c16 - 4g - e) on/below the diagonal, else 0.
+  float cst[4], Ddg[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    cst[e] = gamma_pow(lg, 3 - e);
+    const int d = c16 - 4 * g - e;
+    Ddg[e] = d >= 0 ? gamma_pow(lg, d) : 0.0f;
+  }
+  const int lane_off = c16 - 4 * g - 3;
 
   // ---- carried state: R_0 = state_in (or zeros), kept as fp32 accumulators
   f32x4 Racc[F::RM][4];
@@ -145,54 +184,56 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       }
   };
 
-  uint4 kreg[F::KPT];
-  uint4 vreg[F::VPT];
+  // Global loads go through buffer resources whose size ends at the chunk's
+  // last valid row: rows past it read as zero (no branches, so the compiler
+  // can count outstanding loads and keep the next chunk's loads in flight).
+  u32x4 kreg[F::KPT];
+  u32x4 vreg[F::VPT];
   bf16x8 Qreg[F::NQ][F::KS];
+  // Staging map: groups of 8 lanes read 128 contiguous bytes (a full cache line)
+  // per instruction; a thread's pieces are 128 bytes (K) or one row (V) apart, so
+  // the per-piece offsets fit the instructions' immediate offset field.
+  const int grp = tid >> 3, gl = tid & 7;
+  const uint32_t koff = static_cast<uint32_t>(grp * 8 * F::KPT + gl) * 16u;  // + 128 r
+  const int vrow0 = grp * F::VPT;                                            // rows vrow0 + r
+  const uint32_t voff = static_cast<uint32_t>(vrow0) * vrow + 16u * gl;      // + r * vrow
+  float zfull[F::VPT];  // gamma^(C-1-row) for full chunks
+#pragma unroll
+  for (int r = 0; r < F::VPT; ++r) zfull[r] = vrow0 + r < C ? gamma_pow(lg, C - 1 - (vrow0 + r)) : 0.0f;
 
   auto load_kv = [&](int s1, int Ln) {
+    const rsrc_t rk = make_rsrc(kh + static_cast<long>(s1) * DK, static_cast<uint32_t>(Ln) * DK * 2u);
 #pragma unroll
-    for (int r = 0; r < F::KPT; ++r) {
-      const int p = tid + kThreads * r;
-      const int row = p / (DK / 8), c8 = p % (DK / 8);
-      kreg[r] = row < Ln ? *reinterpret_cast<const uint4*>(kh + static_cast<long>(s1 + row) * DK + 8 * c8)
-                         : make_uint4(0, 0, 0, 0);
-    }
+    for (int r = 0; r < F::KPT; ++r) kreg[r] = buffer_load16(rk, koff + 128u * r);
+    const rsrc_t rv = make_rsrc(vh + static_cast<long>(s1) * dv, Ln > 0 ? static_cast<uint32_t>(Ln - 1) * vrow + kTN * 2u : 0u);
 #pragma unroll
-    for (int r = 0; r < F::VPT; ++r) {
-      const int p = tid + kThreads * r;
-      const int row = p / (kTN / 8), c8 = p % (kTN / 8);
-      vreg[r] = row < Ln ? *reinterpret_cast<const uint4*>(vh + static_cast<long>(s1 + row) * dv + 8 * c8)
-                         : make_uint4(0, 0, 0, 0);
-    }
+    for (int r = 0; r < F::VPT; ++r) vreg[r] = buffer_load16(rv, voff + vrow * r);
   };
   auto store_kv = [&](int Ln) {
 #pragma unroll
     for (int r = 0; r < F::KPT; ++r) {
-      const int p = tid + kThreads * r;
+      const int p = grp * 8 * F::KPT + 8 * r + gl;
       const int row = p / (DK / 8), c8 = p % (DK / 8);
-      *reinterpret_cast<uint4*>(&Ks[row * F::KLD + 8 * c8]) = kreg[r];
+      *reinterpret_cast<u32x4*>(&Ks[row * F::KLD + 8 * c8]) = kreg[r];
     }
 #pragma unroll
     for (int r = 0; r < F::VPT; ++r) {
-      const int p = tid + kThreads * r;
-      const int row = p / (kTN / 8), c8 = p % (kTN / 8);
-      *reinterpret_cast<uint4*>(&Vs[row * F::VLD + 8 * c8]) = vreg[r];
+      const int row = vrow0 + r;
+      *reinterpret_cast<u32x4*>(&Vs[row * F::VLD + 8 * gl]) = vreg[r];
       // zeta_row = gamma^(L-1-row) scales V for the state update (0 past the chunk end)
-      const float z = row < Ln ? gamma_pow(lg, Ln - 1 - row) : 0.0f;
+      const float z = Ln == C ? zfull[r] : (row < Ln ? gamma_pow(lg, Ln - 1 - row) : 0.0f);
       const bf16x8 vb = __builtin_bit_cast(bf16x8, vreg[r]);
       const f32x8 vf = __builtin_convertvector(vb, f32x8) * z;
-      *reinterpret_cast<bf16x8*>(&Vz[row * F::VLD + 8 * c8]) = __builtin_convertvector(vf, bf16x8);
+      *reinterpret_cast<bf16x8*>(&Vz[row * F::VLD + 8 * gl]) = __builtin_convertvector(vf, bf16x8);
     }
   };
   auto load_q = [&](int s1, int Ln) {
+    const rsrc_t rq = make_rsrc(qh + static_cast<long>(s1) * DK, static_cast<uint32_t>(Ln) * DK * 2u);
 #pragma unroll
     for (int qi = 0; qi < F::NQ; ++qi) {
-      const int row = 16 * qblk[qi] + c16;
+      const uint32_t rowoff = static_cast<uint32_t>(16 * qblk[qi] + c16) * DK * 2u + 16u * g;
 #pragma unroll
-      for (int s = 0; s < F::KS; ++s) {
-        Qreg[qi][s] = row < Ln ? *reinterpret_cast<const bf16x8*>(qh + static_cast<long>(s1 + row) * DK + 32 * s + 8 * g)
-                               : bf16x8{};
-      }
+      for (int s = 0; s < F::KS; ++s) Qreg[qi][s] = __builtin_bit_cast(bf16x8, buffer_load16(rq, rowoff + 64u * s));
     }
   };
 
@@ -211,52 +252,61 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     const int s1 = s0 + C;
     const bool has_next = s1 < Tn;
     const int Ln = has_next ? min(C, Tn - s1) : 0;
-    if (has_next) load_kv(s1, Ln);
+    // issued unconditionally (an empty buffer past the end reads zeros) so that
+    // the wait counters stay exact and the loads overlap this chunk's work
+    load_kv(s1, Ln);
 
     // ================= phase A: outputs of this chunk =================
-    f32x4 Ox[F::NQ][4];
-    f32x4 Op[F::NQ][4];
+    // cross-chunk term first: O = gamma^(j+1) (Q R_i), then P V accumulates on top
+    f32x4 O[F::NQ][4];
+    {
+      bf16x8 rb[2][4];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) rb[0][nb] = lds_read16(&Rt[(16 * nb + c16) * F::RLD + 8 * g]);
+#pragma unroll
+      for (int s = 0; s < F::KS; ++s) {
+        if (s + 1 < F::KS) {
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            rb[(s + 1) & 1][nb] = lds_read16(&Rt[(16 * nb + c16) * F::RLD + 32 * (s + 1) + 8 * g]);
+        }
+#pragma unroll
+        for (int qi = 0; qi < F::NQ; ++qi)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            O[qi][nb] = mfma(Qreg[qi][s], rb[s & 1][nb], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : O[qi][nb]);
+      }
+    }
 #pragma unroll
     for (int qi = 0; qi < F::NQ; ++qi)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        Ox[qi][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Op[qi][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 4; ++i) {
+        const float xi = gamma_pow(lg, 16 * qblk[qi] + 4 * g + i + 1);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) O[qi][nb][i] *= xi;
       }
-    // cross-chunk term Q R_i (B operand = rows of R^T, 16 bytes per lane)
+
+    // intra-chunk term: key steps of 32 keys on or below the diagonal
 #pragma unroll
-    for (int s = 0; s < F::KS; ++s) {
-      bf16x8 rb[4];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) rb[nb] = lds_read16(&Rt[(16 * nb + c16) * F::RLD + 32 * s + 8 * g]);
-#pragma unroll
-      for (int qi = 0; qi < F::NQ; ++qi)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) Ox[qi][nb] = mfma(Qreg[qi][s], rb[nb], Ox[qi][nb]);
-    }
-    // intra-chunk term: key steps of 32 keys below the diagonal
-    const int qmax = qblk[F::NQ - 1] > qblk[0] ? qblk[F::NQ - 1] : qblk[0];
-    for (int sp = 0; 2 * sp <= qmax; ++sp) {
-      f32x4 St[F::NQ][2];
-#pragma unroll
-      for (int qi = 0; qi < F::NQ; ++qi) {
-        St[qi][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        St[qi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+    for (int sp = 0; sp < NSP; ++sp) {
       bool need0[F::NQ], need1[F::NQ];
+      bool any = false;
 #pragma unroll
       for (int qi = 0; qi < F::NQ; ++qi) {
         need0[qi] = qblk[qi] >= 2 * sp;
         need1[qi] = qblk[qi] >= 2 * sp + 1;
+        any = any || need0[qi];
       }
+      if (!any) continue;
+      f32x4 St[F::NQ][2];
 #pragma unroll
       for (int s = 0; s < F::KS; ++s) {
         const bf16x8 ka = lds_read16(&Ks[(32 * sp + c16) * F::KLD + 32 * s + 8 * g]);
         const bf16x8 kb = lds_read16(&Ks[(32 * sp + 16 + c16) * F::KLD + 32 * s + 8 * g]);
 #pragma unroll
         for (int qi = 0; qi < F::NQ; ++qi) {
-          if (need0[qi]) St[qi][0] = mfma(ka, Qreg[qi][s], St[qi][0]);
-          if (need1[qi]) St[qi][1] = mfma(kb, Qreg[qi][s], St[qi][1]);
+          if (need0[qi]) St[qi][0] = mfma(ka, Qreg[qi][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : St[qi][0]);
+          if (need1[qi]) St[qi][1] = mfma(kb, Qreg[qi][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : St[qi][1]);
         }
       }
       // V operands (keys 32sp+4g+e and 32sp+16+4g+e), shared by both query blocks
@@ -271,40 +321,45 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
       for (int qi = 0; qi < F::NQ; ++qi) {
         if (!need0[qi]) continue;
-        const int j = 16 * qblk[qi] + c16;  // query row of this lane
         f32x8 p;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int t = 32 * sp + 4 * g + (e & 3) + 16 * (e >> 2);
-          const int d = j - t;
-          const float sv = e < 4 ? St[qi][0][e & 3] : St[qi][1][e & 3];
-          p[e] = d > 0 ? sv * exp2f(static_cast<float>(d) * lg) : (d == 0 ? sv : 0.0f);
+        for (int h = 0; h < 2; ++h) {
+          const int m = qblk[qi] - (2 * sp + h);  // wave-uniform
+          const float boff = m > 0 ? exp2f(static_cast<float>(16 * m + lane_off) * lg) : 0.0f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float f;
+            if (m > 0) f = boff * cst[e];
+            else if (m == 0) f = Ddg[e];
+            else f = 0.0f;
+            p[4 * h + e] = (h == 0 ? St[qi][0][e] : (need1[qi] ? St[qi][1][e] : 0.0f)) * f;
+          }
         }
         const bf16x8 pa = __builtin_convertvector(p, bf16x8);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) Op[qi][nb] = mfma(pa, vb[nb], Op[qi][nb]);
+        for (int nb = 0; nb < 4; ++nb) O[qi][nb] = mfma(pa, vb[nb], O[qi][nb]);
       }
     }
-    // combine and store: Y = P V + gamma^(j+1) Q R
+    // Q of the next chunk: issued before this chunk's Y stores so that the
+    // next phase A waits on these loads only, not on the stores
+    load_q(s1, Ln);
+    // store Y rows (rows past the chunk end fall outside the buffer and are dropped)
+    {
+      const rsrc_t ry = make_rsrc(yh + static_cast<long>(s0) * dv, static_cast<uint32_t>(L - 1) * vrow + kTN * 2u);
 #pragma unroll
-    for (int qi = 0; qi < F::NQ; ++qi) {
+      for (int qi = 0; qi < F::NQ; ++qi)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * qblk[qi] + 4 * g + i;
-        const float xi = exp2f(static_cast<float>(row + 1) * lg);
-        if (row < L) {
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t roff = static_cast<uint32_t>(16 * qblk[qi] + 4 * g + i) * vrow + 2u * c16;
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            yh[static_cast<long>(s0 + row) * dv + 16 * nb + c16] = f32_to_bf16(fmaf(xi, Ox[qi][nb][i], Op[qi][nb][i]));
+          for (int nb = 0; nb < 4; ++nb) buffer_store2(ry, roff + 32u * nb, f32_to_bf16(O[qi][nb][i]));
         }
-      }
     }
-    if (has_next) load_q(s1, Ln);
     __syncthreads();  // all waves are done reading R^T, V and K for outputs
 
     // ================= phase B: state update =================
     {
-      const float gL = gamma_pow(lg, L);
+      const float gL = L == C ? gamma_pow(lg, C) : gamma_pow(lg, L);
 #pragma unroll
       for (int mb = 0; mb < F::RM; ++mb)
 #pragma unroll
@@ -352,26 +407,29 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   }
 }
 
-template <int CT, int DK>
+template <int CT, int DK, int NW>
 hipError_t launch_cfg(const void* q, const void* k, const void* v, const float* state_in, float* state_out, void* y,
                       int B, int H, int Tn, int dv, int C, const HeadDecay& hd, const HeadGroup& g, hipStream_t s) {
   const int ntiles = dv / kTN;
   const int total = B * g.nh * ntiles;
-  hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK>), dim3(total), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, NW>), dim3(total), dim3(64 * NW), 0, s,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), state_in, state_out, static_cast<uint16_t*>(y), hd, H, g.h0,
                      g.nh, Tn, dv, C, ntiles);
   return hipGetLastError();
 }
 
+// 64-token tiles run 4 waves (one query block each); 128-token tiles run 8
+// waves (two per SIMD) when d_k allows 32 state rows per wave.
 template <int CT>
 hipError_t launch_ct(const void* q, const void* k, const void* v, const float* state_in, float* state_out, void* y,
                      int B, int H, int Tn, int dk, int dv, int C, const HeadDecay& hd, const HeadGroup& g,
                      hipStream_t s) {
+  constexpr int NW = CT == 128 ? 8 : 4;
   switch (dk) {
-    case 64: return launch_cfg<CT, 64>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, s);
-    case 128: return launch_cfg<CT, 128>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, s);
-    default: return launch_cfg<CT, 256>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, s);
+    case 64: return launch_cfg<CT, 64, 4>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, s);
+    case 128: return launch_cfg<CT, 128, NW>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, s);
+    default: return launch_cfg<CT, 256, NW>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, s);
   }
 }
 
