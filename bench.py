@@ -1,0 +1,252 @@
+"""Benchmark of the retention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one chunkwise retention forward (retention_chunkwise_fwd: intra-chunk
+(Q K^T .* D) V, cross-chunk Q R gamma^(j+1), state update, carried fp32 state)
+over one batch of the 1.3B-scale layer workload: B=4, H=8, T=2048, d_k=256,
+d_v=512, bf16, C=64, gamma_h = 1 - 2^(-5-h), seeded synthetic inputs.  Inputs
+are resident in HBM before timing; four input sets rotate so that each step
+reads cold data (one set, 201 MB, would fit in the 256 MB last-level cache).
+
+The recurrent decode step (retention_recurrent_step, batch 128, H=16, fp32
+256x512 state per head, 1000 chained steps) is measured in the same run and
+reported in the "decode" object.
+
+Prints ONE JSON line.  The roofline of the chunkwise kernel uses algorithmic
+HBM bytes (bf16 Q, K, V in and Y out: 3072 bytes per head-token) over the
+kernel's average duration measured with HIP events on the launch stream.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def head_token_flops(dk, dv, C):
+    # two d_k x d_v contractions (cross term, state update) + causal intra-chunk
+    # Q K^T and P V: 4 dk dv + (C+1)(dk+dv) flops per head-token
+    return 4 * dk * dv + (C + 1) * (dk + dv)
+
+
+def source_digest(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(name, kernel_src):
+    """HBM bytes per launch from committed rocprofv3 counter runs (FETCH_SIZE +
+    WRITE_SIZE, copy-calibrated), if they were taken on the current kernel
+    source; else None."""
+    from retnet_retention_chunkwise_amd.rocprof_summary import read_traffic_file
+
+    p = os.path.join(PROFILES, name)
+    if not os.path.exists(p):
+        return None
+    rec = read_traffic_file(p)
+    if rec.get("kernel_source_sha256_16") != source_digest(kernel_src):
+        return None
+    try:
+        return float(rec["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline_chunkwise(wl, sample_B, sample_T):
+    """The fp64 oracle (recurrent form) on a bounded sample: the first sample_B
+    batch elements, all heads, the first sample_T tokens.  Returns tokens/s in
+    the GPU metric's unit (a token counts once across all heads)."""
+    import torch
+
+    import oracle
+    from retnet_retention_chunkwise_amd.workloads import make_inputs
+
+    q, k, v = make_inputs(sample_B, wl.H, sample_T, wl.dk, wl.dv, wl.dtype, seed=0)
+    g = torch.tensor(wl.gammas, dtype=torch.float32)
+    t0 = time.perf_counter()
+    oracle.recurrent(q, k, v, g)
+    dt = time.perf_counter() - t0
+    return sample_B * sample_T / dt, dt, torch.get_num_threads()
+
+
+def cpu_baseline_decode(wl, n_steps, n_batch):
+    import torch
+
+    import oracle
+    from retnet_retention_chunkwise_amd.workloads import make_decode_inputs
+
+    q, k, v, s0 = make_decode_inputs(n_batch, wl.H, wl.dk, wl.dv, n_steps, wl.dtype, seed=0)
+    g = torch.tensor(wl.gammas, dtype=torch.float32)
+    S = s0
+    t0 = time.perf_counter()
+    for n in range(n_steps):
+        _, S = oracle.recurrent_step(q[n], k[n], v[n], g, S)
+    dt = time.perf_counter() - t0
+    # steps/s of the full batch: the sample covers n_batch of wl.B sequences
+    return n_steps / dt * n_batch / wl.B, dt, torch.get_num_threads()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (counter calibration under rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import retnet_retention_chunkwise_amd as ret
+    from retnet_retention_chunkwise_amd.workloads import WORKLOADS, make_decode_inputs, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    ret.load()
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ------------------------------------------------ chunkwise forward
+    wl = WORKLOADS["layer1p3b"]
+    n_rot = 4
+    sets = []
+    for r in range(n_rot):
+        q, k, v = make_inputs(wl.B, wl.H, wl.T, wl.dk, wl.dv, wl.dtype, seed=r)
+        sets.append((q.to(dev), k.to(dev), v.to(dev), torch.empty(wl.B, wl.H, wl.T, wl.dv, dtype=q.dtype, device=dev)))
+    g = list(wl.gammas)
+    for i in range(args.warmup):
+        qd, kd, vd, yd = sets[i % n_rot]
+        ret.chunkwise_fwd(qd, kd, vd, g, wl.C, y=yd, state_out=False)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        qd, kd, vd, yd = sets[i % n_rot]
+        ret.chunkwise_fwd(qd, kd, vd, g, wl.C, y=yd, state_out=False)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    tokens = wl.B * wl.T
+    value = tokens / (ms_per_step * 1e-3)
+    head_tokens = wl.B * wl.H * wl.T
+    alg_bytes = head_tokens * (2 * wl.dk + 2 * wl.dk + 2 * wl.dv + 2 * wl.dv)  # q, k, v in, y out (bf16)
+    alg_flops = head_tokens * head_token_flops(wl.dk, wl.dv, wl.C)
+    achieved_gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved_tflops = alg_flops / (ms_per_step * 1e-3) / 1e12
+    kernel_src = os.path.join(ROOT, "retnet_retention_chunkwise_amd", "csrc", "chunkwise_mfma.hip")
+    traffic = load_traffic("chunkwise_mfma_layer1p3b_traffic.txt", kernel_src)
+    del sets
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------ recurrent decode
+    dw = WORKLOADS["decode"]
+    dq, dk_, dv_, s0 = make_decode_inputs(dw.B, dw.H, dw.dk, dw.dv, args.decode_steps, dw.dtype, seed=0)
+    dq, dk_, dv_ = dq.to(dev), dk_.to(dev), dv_.to(dev)
+    state = s0.to(dev)
+    ydec = torch.empty(dw.B, dw.H, dw.dv, dtype=dq.dtype, device=dev)
+    gd = list(dw.gammas)
+    for n in range(10):  # warm-up steps (the state keeps evolving; the timed steps continue from it)
+        m = n % args.decode_steps
+        ret.recurrent_step(dq[m], dk_[m], dv_[m], gd, state, y=ydec)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for n in range(args.decode_steps):
+        ret.recurrent_step(dq[n], dk_[n], dv_[n], gd, state, y=ydec)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1)
+    dec_us_step = dec_ms * 1e3 / args.decode_steps
+    state_bytes = dw.B * dw.H * dw.dk * dw.dv * 4
+    dec_bytes = 2 * state_bytes + dw.B * dw.H * (2 * dw.dk + 2 * dw.dk + 2 * dw.dv + 2 * dw.dv)
+    dec_gbs = dec_bytes / (dec_us_step * 1e-6) / 1e9
+    dec_src = os.path.join(ROOT, "retnet_retention_chunkwise_amd", "csrc", "recurrent_step.hip")
+    dec_traffic = load_traffic("recurrent_step_decode_traffic.txt", dec_src)
+    del dq, dk_, dv_, state
+    torch.cuda.empty_cache()
+
+    out = {
+        "metric": "retention tokens/sec (chunkwise fwd) + decode steps/sec; % MFMA / HBM peak",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)/sqrt(dk) inputs, 4 rotating input sets)",
+        "config": {"workload": "layer1p3b: chunkwise fwd B=4 H=8 T=2048 dk=256 dv=512 bf16 C=64, "
+                               "gamma_h=1-2^(-5-h), fp32 state",
+                   "global_batch": wl.B, "seq_len": wl.T, "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved_gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "kernel": "chunkwise_mfma_kernel<64,256,4>",
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "algorithmic_flops_per_launch": alg_flops,
+            "mfma_tflops": achieved_tflops,
+            "mfma_frac": achieved_tflops / BF16_PEAK_TFLOPS,
+        },
+        "decode": {
+            "workload": "recurrent step: batch 128, H=16, fp32 state 256x512 per head, bf16 q/k/v, "
+                        f"{args.decode_steps} chained steps",
+            "steps_per_s": 1e3 * args.decode_steps / dec_ms,
+            "us_per_step": dec_us_step,
+            "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dec_gbs / HBM_PEAK_GBS, "traffic": dec_traffic,
+                         "algorithmic_bytes_per_launch": dec_bytes},
+        },
+    }
+    if not args.no_cpu_baseline:
+        sample_B = int(os.environ.get("RET_CPU_SAMPLE_B", str(wl.B)))
+        sample_T = int(os.environ.get("RET_CPU_SAMPLE_T", str(wl.T)))
+        v_cpu, dt, cores = cpu_baseline_chunkwise(wl, sample_B, sample_T)
+        out["cpu_baseline"] = {
+            "value": v_cpu, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 recurrent-form oracle on {sample_B} of {wl.B} batch elements x all {wl.H} heads x "
+                      f"{sample_T} of {wl.T} tokens of the layer1p3b workload: {dt:.1f} s",
+        }
+        dsteps = int(os.environ.get("RET_CPU_DECODE_STEPS", "64"))
+        dbatch = int(os.environ.get("RET_CPU_DECODE_BATCH", "16"))
+        v_dec, ddt, _ = cpu_baseline_decode(dw, dsteps, dbatch)
+        out["decode"]["cpu_baseline"] = {
+            "value": v_dec, "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 oracle decode steps, {dbatch} of {dw.B} sequences x {dw.H} heads, {dsteps} steps "
+                      f"({ddt:.1f} s), scaled to the full batch",
+        }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,129 @@
+"""Summaries of rocprofv3 CSV output for the libretention kernels.
+
+    python -m retnet_retention_chunkwise_amd.rocprof_summary stats <kernel_stats.csv> [--cmd "..."]
+    python -m retnet_retention_chunkwise_amd.rocprof_summary traffic --fetch <dir> --write <dir> \
+        --kernel <name substring> --source <kernel .hip> --copy-mib <N> [--cmd "..."]
+
+`stats` turns a `--kernel-trace --stats` kernel_stats.csv into a short text
+table.  `traffic` turns two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs into
+HBM bytes per launch of one kernel, calibrated against a plain copy of
+`--copy-mib` MiB measured in the same runs (bytes = counter * known copy bytes /
+copy's counter), and records the sha256 of the kernel source so that a reader
+can tell whether the figures still describe the current kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import os
+import sys
+
+
+def _short(name: str, width: int = 70) -> str:
+    n = name.replace("(anonymous namespace)::", "")
+    return n if len(n) <= width else n[: width - 3] + "..."
+
+
+def stats_table(path: str, cmd: str = "") -> str:
+    rows = list(csv.DictReader(open(path)))
+    lines = []
+    if cmd:
+        lines.append(f"command: {cmd}")
+    lines.append(f"{'kernel':72s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}")
+    for r in rows:
+        lines.append(f"{_short(r['Name'], 72):72s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}")
+    return "\n".join(lines) + "\n"
+
+
+def _per_dispatch(directory: str, counter: str):
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {directory}")
+    acc = collections.defaultdict(float)
+    names = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (f, r["Dispatch_Id"])
+            acc[key] += float(r["Counter_Value"])
+            names[key] = r["Kernel_Name"]
+    return [(names[k], v) for k, v in acc.items()]
+
+
+def _mean_for(entries, substr):
+    vals = [v for n, v in entries if substr in n]
+    if not vals:
+        raise ValueError(f"no dispatch of a kernel matching '{substr}'")
+    return sum(vals) / len(vals), len(vals)
+
+
+def traffic(fetch_dir, write_dir, kernel, source, copy_mib, copy_substr="copy", cmd=""):
+    f_entries = _per_dispatch(fetch_dir, "FETCH_SIZE")
+    w_entries = _per_dispatch(write_dir, "WRITE_SIZE")
+    k_fetch, n_f = _mean_for(f_entries, kernel)
+    k_write, n_w = _mean_for(w_entries, kernel)
+    c_fetch, _ = _mean_for(f_entries, copy_substr)
+    c_write, _ = _mean_for(w_entries, copy_substr)
+    copy_bytes = copy_mib * 1024 * 1024
+    f_scale = copy_bytes / (c_fetch * 1024.0)
+    w_scale = copy_bytes / (c_write * 1024.0)
+    rd = k_fetch * 1024.0 * f_scale
+    wr = k_write * 1024.0 * w_scale
+    sha = hashlib.sha256(open(source, "rb").read()).hexdigest()[:16]
+    lines = []
+    if cmd:
+        lines.append(f"command: {cmd}")
+    lines += [
+        f"kernel: {kernel}",
+        f"kernel_source: {os.path.basename(source)}",
+        f"kernel_source_sha256_16: {sha}",
+        f"dispatches_averaged: fetch {n_f}, write {n_w}",
+        f"FETCH_SIZE_KiB_per_launch: {k_fetch:.1f}",
+        f"WRITE_SIZE_KiB_per_launch: {k_write:.1f}",
+        f"copy_calibration: {copy_mib} MiB copy read {c_fetch:.1f} KiB / wrote {c_write:.1f} KiB "
+        f"-> factors read {f_scale:.4f}, write {w_scale:.4f}",
+        f"read_bytes_per_launch: {rd:.0f}",
+        f"write_bytes_per_launch: {wr:.0f}",
+        f"traffic_bytes_per_launch: {rd + wr:.0f}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
+def read_traffic_file(path: str):
+    """Parse a `traffic` summary back into a dict (used by bench.py)."""
+    out = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            out[k.strip()] = v.strip()
+    return out
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd_name", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--cmd", default="")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--source", required=True)
+    t.add_argument("--copy-mib", type=float, required=True)
+    t.add_argument("--copy-kernel", default="copy")
+    t.add_argument("--cmd", default="")
+    a = ap.parse_args(argv)
+    if a.cmd_name == "stats":
+        sys.stdout.write(stats_table(a.csv, a.cmd))
+    else:
+        sys.stdout.write(traffic(a.fetch, a.write, a.kernel, a.source, a.copy_mib, a.copy_kernel, a.cmd))
+
+
+if __name__ == "__main__":
+    main()
