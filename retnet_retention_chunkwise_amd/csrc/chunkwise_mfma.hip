@@ -7,28 +7,31 @@
 //   Y_[i]   = ((Q_[i] K_[i]^T) .* D_L) V_[i] + diag(gamma^(j+1)) Q_[i] R_i
 //   R_(i+1) = gamma^L R_i + K_[i]^T (diag(gamma^(L-1-j)) V_[i])
 //
-// Work decomposition (one workgroup = 4 waves = 256 threads):
-//   * a workgroup owns one (batch, head, tile of 64 value columns) and walks the
-//     chunks of the sequence in order; the 8 column tiles of a head are mapped
-//     to one XCD so that their shared Q/K reads hit the same L2;
-//   * the fp32 state tile R[d_k x 64] lives in MFMA accumulators for the whole
-//     sequence: wave w owns rows [w*d_k/4, (w+1)*d_k/4);
-//   * per chunk, wave w owns query blocks of 16 rows ({w, 7-w} for 128-token
+// Work decomposition.  A workgroup owns one (batch, head, tile of 64 value
+// columns) and walks the chunks of the sequence in order; the 8 column tiles
+// of a head are placed on one XCD so that their shared Q/K reads hit one L2.
+// The workgroup has 8 waves in two roles, one of each per SIMD (waves w and
+// w+4 share a SIMD), so that each role's memory and LDS latencies are covered
+// by the other role's instructions:
+//   * output waves 0..3 own 16-row query blocks ({w, 7-w} for 128-token
 //     chunks, which balances the causal triangle; {w} for 64-token chunks).
-//     Its Q rows are loaded from global memory straight into MFMA operand
-//     registers and serve both S^T = K Q^T and the cross term Q R;
-//   * S^T stays in registers: its accumulator layout is, up to a permutation of
-//     the key index, the A-operand layout that P = S .* D needs for P V, so the
-//     decay mask is applied in registers and P never touches LDS;
-//   * K and the 64-column V tile are staged in LDS (row-major); the state
-//     update contracts over tokens and reads K^T and (gamma^(L-1-j) V) with
-//     ds_read_b64_tr_b16, the gfx950 transposing LDS load;
-//   * R^T is kept in LDS as bf16 for the cross term's B operand and rewritten
-//     after every update;
-//   * the next chunk's K/V (and Q) are loaded into registers while the current
-//     chunk computes; three barriers per chunk separate the phases.
-// Decay factors gamma^d are generated in registers from log2(gamma) (exp2),
-// with gamma^0 forced to 1.
+//     Their Q rows are loaded from global memory straight into MFMA operand
+//     registers and serve both S^T = K Q^T and the cross term Q R.  S^T stays
+//     in registers: its accumulator layout is, up to a permutation of the key
+//     index, the A-operand layout that P = S .* D needs for P V, so the decay
+//     mask is applied in registers and P never touches LDS.  V is read with
+//     the same key permutation through ds_read_b64_tr_b16, the gfx950
+//     transposing LDS load.  The cross term reads R^T (bf16) from LDS.
+//   * state waves 4..7 own d_k/4 rows of the fp32 state tile R[d_k x 64],
+//     kept in MFMA accumulators for the whole sequence.  They run the update
+//     R <- gamma^L R + K^T (zeta V) (K^T and zeta V through the transposing
+//     load), publish R^T to LDS, and stage the next chunk's K and V tiles
+//     (global loads into registers during the chunk, LDS writes after it).
+// Per chunk: [outputs | update] barrier [R^T and next K/V written] barrier.
+// Every global access goes through a buffer resource that ends at the
+// chunk's last valid row, so rows past the end read as zero / are dropped
+// without branches.  Decay factors gamma^d come from log2(gamma) with
+// gamma^0 forced to 1.
 #include "common.h"
 #include "kernels.h"
 
@@ -78,31 +81,30 @@ __device__ __forceinline__ void buffer_store2(rsrc_t r, uint32_t off, uint16_t x
   __builtin_amdgcn_raw_buffer_store_b16(x, r, static_cast<int>(off), 0, 0);
 }
 
-template <int CT, int DK, int NW>
+template <int CT, int DK>
 struct Cfg {
-  static constexpr int kThreads = 64 * NW;
+  static constexpr int kThreads = 512;         // 4 output waves + 4 state waves
+  static constexpr int kStageThreads = 256;    // the state waves stage K/V
   static constexpr int KLD = DK + 8;           // K row stride in LDS (elements)
   static constexpr int VLD = kTN + 8;          // V / zeta*V row stride
   static constexpr int RLD = DK + 8;           // R^T row stride
-  static constexpr int NQ = CT / (16 * NW);    // query blocks per wave
-  static constexpr int RM = DK / (16 * NW);    // 16-row state blocks per wave
+  static constexpr int NQ = CT / 64;           // query blocks per output wave
+  static constexpr int RM = DK / 64;           // 16-row state blocks per state wave
   static constexpr int KS = DK / 32;           // k-steps over d_k
-  static constexpr int KPT = CT * DK / 8 / kThreads;   // 16-byte K pieces per thread
-  static constexpr int VPT = CT * kTN / 8 / kThreads;  // 16-byte V pieces per thread
-  static_assert(NQ >= 1 && NQ <= 2 && RM >= 1, "unsupported wave split");
+  static constexpr int KPT = CT * DK / 8 / kStageThreads;   // 16-byte K pieces per staging thread
+  static constexpr int VPT = CT * kTN / 8 / kStageThreads;  // 16-byte V pieces per staging thread
+  static_assert(NQ >= 1 && NQ <= 2 && RM >= 1, "unsupported tile");
   static_assert(KPT >= 1 && VPT >= 1, "tile too small for the staging split");
 };
 
-template <int CT, int DK, int NW>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(NW / 4, NW / 4))) void
+template <int CT, int DK>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2))) void
 chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                       const uint16_t* __restrict__ v, const float* state_in, float* state_out,
                       uint16_t* __restrict__ y, HeadDecay gam, int H, int h0, int nh, int Tn, int dv, int C,
                       int ntiles) {
-  using F = Cfg<CT, DK, NW>;
-  constexpr int kThreads = F::kThreads;
+  using F = Cfg<CT, DK>;
   constexpr int NSP = CT / 32;  // key steps of 32 keys per chunk tile
-  constexpr int NKB = CT / 16;  // 16-row blocks per chunk tile
   __shared__ __attribute__((aligned(16))) uint16_t Ks[CT * F::KLD];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[CT * F::VLD];
   __shared__ __attribute__((aligned(16))) uint16_t Vz[CT * F::VLD];
@@ -111,6 +113,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar) by construction
+  const int wr = w & 3;                                      // index within the role
   const int c16 = lane & 15;
   const int g = lane >> 4;
 
@@ -134,231 +137,92 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   uint16_t* yh = y + head * Tn * dv + col0;
   const long sbase = head * static_cast<long>(DK) * dv + col0;
   const uint32_t vrow = static_cast<uint32_t>(dv) * 2u;  // bytes per V / Y row
+  const int nchunks = (Tn + C - 1) / C;
 
-  // Query blocks of this wave.  Waves w and w+4 share a SIMD; the pairings
-  // below give every SIMD query blocks {s, 7-s} of a 128-token chunk, which
-  // balances the causal triangle.
-  int qblk[F::NQ];
-  if constexpr (F::NQ == 2) {
-    qblk[0] = w;
-    qblk[1] = 7 - w;
-  } else if constexpr (NW == 8) {
-    qblk[0] = w < 4 ? w : 11 - w;
-  } else {
-    qblk[0] = w;
-  }
-  const int dbase = w * (DK / NW);
-
-  // ---- decay factors that do not depend on the chunk (positions are chunk-relative)
-  // off-diagonal key block kb < qb: gamma^(j-t) = gamma^(16(qb-kb) + c16 - 4g - 3) * cst[t & 3]
-  //   (first exponent >= 1), cst[e] = gamma^(3-e);
-  // diagonal key block kb == qb: Ddg[e] = gamma^(c16 - 4g - e) on/below the diagonal, else 0.
-  float cst[4], Ddg[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    cst[e] = gamma_pow(lg, 3 - e);
-    const int d = c16 - 4 * g - e;
-    Ddg[e] = d >= 0 ? gamma_pow(lg, d) : 0.0f;
-  }
-  const int lane_off = c16 - 4 * g - 3;
-
-  // ---- carried state: R_0 = state_in (or zeros), kept as fp32 accumulators
-  f32x4 Racc[F::RM][4];
-#pragma unroll
-  for (int mb = 0; mb < F::RM; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = dbase + 16 * mb + 4 * g + i;
-        Racc[mb][nb][i] = state_in != nullptr ? state_in[sbase + static_cast<long>(d) * dv + 16 * nb + c16] : 0.0f;
-      }
-
-  auto write_rt = [&]() {
+  if (w >= 4) {
+    // =========================== state waves ===========================
+    const int st = tid - 256;  // staging thread index 0..255
+    const int dbase = wr * (DK / 4);
+    f32x4 Racc[F::RM][4];
 #pragma unroll
     for (int mb = 0; mb < F::RM; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const bf16x4 r = __builtin_convertvector(Racc[mb][nb], bf16x4);
-        *reinterpret_cast<bf16x4*>(&Rt[(16 * nb + c16) * F::RLD + dbase + 16 * mb + 4 * g]) = r;
-      }
-  };
-
-  // Global loads go through buffer resources whose size ends at the chunk's
-  // last valid row: rows past it read as zero (no branches, so the compiler
-  // can count outstanding loads and keep the next chunk's loads in flight).
-  u32x4 kreg[F::KPT];
-  u32x4 vreg[F::VPT];
-  bf16x8 Qreg[F::NQ][F::KS];
-  // Staging map: groups of 8 lanes read 128 contiguous bytes (a full cache line)
-  // per instruction; a thread's pieces are 128 bytes (K) or one row (V) apart, so
-  // the per-piece offsets fit the instructions' immediate offset field.
-  const int grp = tid >> 3, gl = tid & 7;
-  const uint32_t koff = static_cast<uint32_t>(grp * 8 * F::KPT + gl) * 16u;  // + 128 r
-  const int vrow0 = grp * F::VPT;                                            // rows vrow0 + r
-  const uint32_t voff = static_cast<uint32_t>(vrow0) * vrow + 16u * gl;      // + r * vrow
-  float zfull[F::VPT];  // gamma^(C-1-row) for full chunks
-#pragma unroll
-  for (int r = 0; r < F::VPT; ++r) zfull[r] = vrow0 + r < C ? gamma_pow(lg, C - 1 - (vrow0 + r)) : 0.0f;
-
-  auto load_kv = [&](int s1, int Ln) {
-    const rsrc_t rk = make_rsrc(kh + static_cast<long>(s1) * DK, static_cast<uint32_t>(Ln) * DK * 2u);
-#pragma unroll
-    for (int r = 0; r < F::KPT; ++r) kreg[r] = buffer_load16(rk, koff + 128u * r);
-    const rsrc_t rv = make_rsrc(vh + static_cast<long>(s1) * dv, Ln > 0 ? static_cast<uint32_t>(Ln - 1) * vrow + kTN * 2u : 0u);
-#pragma unroll
-    for (int r = 0; r < F::VPT; ++r) vreg[r] = buffer_load16(rv, voff + vrow * r);
-  };
-  auto store_kv = [&](int Ln) {
-#pragma unroll
-    for (int r = 0; r < F::KPT; ++r) {
-      const int p = grp * 8 * F::KPT + 8 * r + gl;
-      const int row = p / (DK / 8), c8 = p % (DK / 8);
-      *reinterpret_cast<u32x4*>(&Ks[row * F::KLD + 8 * c8]) = kreg[r];
-    }
-#pragma unroll
-    for (int r = 0; r < F::VPT; ++r) {
-      const int row = vrow0 + r;
-      *reinterpret_cast<u32x4*>(&Vs[row * F::VLD + 8 * gl]) = vreg[r];
-      // zeta_row = gamma^(L-1-row) scales V for the state update (0 past the chunk end)
-      const float z = Ln == C ? zfull[r] : (row < Ln ? gamma_pow(lg, Ln - 1 - row) : 0.0f);
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, vreg[r]);
-      const f32x8 vf = __builtin_convertvector(vb, f32x8) * z;
-      *reinterpret_cast<bf16x8*>(&Vz[row * F::VLD + 8 * gl]) = __builtin_convertvector(vf, bf16x8);
-    }
-  };
-  auto load_q = [&](int s1, int Ln) {
-    const rsrc_t rq = make_rsrc(qh + static_cast<long>(s1) * DK, static_cast<uint32_t>(Ln) * DK * 2u);
-#pragma unroll
-    for (int qi = 0; qi < F::NQ; ++qi) {
-      const uint32_t rowoff = static_cast<uint32_t>(16 * qblk[qi] + c16) * DK * 2u + 16u * g;
-#pragma unroll
-      for (int s = 0; s < F::KS; ++s) Qreg[qi][s] = __builtin_bit_cast(bf16x8, buffer_load16(rq, rowoff + 64u * s));
-    }
-  };
-
-  // ---- prologue: chunk 0 into LDS and registers
-  {
-    const int L0 = min(C, Tn);
-    load_kv(0, L0);
-    load_q(0, L0);
-    write_rt();
-    store_kv(L0);
-  }
-  __syncthreads();
-
-  for (int s0 = 0; s0 < Tn; s0 += C) {
-    const int L = min(C, Tn - s0);
-    const int s1 = s0 + C;
-    const bool has_next = s1 < Tn;
-    const int Ln = has_next ? min(C, Tn - s1) : 0;
-    // issued unconditionally (an empty buffer past the end reads zeros) so that
-    // the wait counters stay exact and the loads overlap this chunk's work
-    load_kv(s1, Ln);
-
-    // ================= phase A: outputs of this chunk =================
-    // cross-chunk term first: O = gamma^(j+1) (Q R_i), then P V accumulates on top
-    f32x4 O[F::NQ][4];
-    {
-      bf16x8 rb[2][4];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) rb[0][nb] = lds_read16(&Rt[(16 * nb + c16) * F::RLD + 8 * g]);
-#pragma unroll
-      for (int s = 0; s < F::KS; ++s) {
-        if (s + 1 < F::KS) {
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            rb[(s + 1) & 1][nb] = lds_read16(&Rt[(16 * nb + c16) * F::RLD + 32 * (s + 1) + 8 * g]);
-        }
-#pragma unroll
-        for (int qi = 0; qi < F::NQ; ++qi)
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            O[qi][nb] = mfma(Qreg[qi][s], rb[s & 1][nb], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : O[qi][nb]);
-      }
-    }
-#pragma unroll
-    for (int qi = 0; qi < F::NQ; ++qi)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float xi = gamma_pow(lg, 16 * qblk[qi] + 4 * g + i + 1);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) O[qi][nb][i] *= xi;
-      }
-
-    // intra-chunk term: key steps of 32 keys on or below the diagonal
-#pragma unroll
-    for (int sp = 0; sp < NSP; ++sp) {
-      bool need0[F::NQ], need1[F::NQ];
-      bool any = false;
-#pragma unroll
-      for (int qi = 0; qi < F::NQ; ++qi) {
-        need0[qi] = qblk[qi] >= 2 * sp;
-        need1[qi] = qblk[qi] >= 2 * sp + 1;
-        any = any || need0[qi];
-      }
-      if (!any) continue;
-      f32x4 St[F::NQ][2];
-#pragma unroll
-      for (int s = 0; s < F::KS; ++s) {
-        const bf16x8 ka = lds_read16(&Ks[(32 * sp + c16) * F::KLD + 32 * s + 8 * g]);
-        const bf16x8 kb = lds_read16(&Ks[(32 * sp + 16 + c16) * F::KLD + 32 * s + 8 * g]);
-#pragma unroll
-        for (int qi = 0; qi < F::NQ; ++qi) {
-          if (need0[qi]) St[qi][0] = mfma(ka, Qreg[qi][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : St[qi][0]);
-          if (need1[qi]) St[qi][1] = mfma(kb, Qreg[qi][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : St[qi][1]);
-        }
-      }
-      // V operands (keys 32sp+4g+e and 32sp+16+4g+e), shared by both query blocks
-      bf16x8 vb[4];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int col = 16 * nb + 4 * (c16 & 3);
-        const s16x4 lo = lds_read_tr(&Vs[(32 * sp + 4 * g + (c16 >> 2)) * F::VLD + col]);
-        const s16x4 hi = lds_read_tr(&Vs[(32 * sp + 16 + 4 * g + (c16 >> 2)) * F::VLD + col]);
-        vb[nb] = join(lo, hi);
-      }
-#pragma unroll
-      for (int qi = 0; qi < F::NQ; ++qi) {
-        if (!need0[qi]) continue;
-        f32x8 p;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int m = qblk[qi] - (2 * sp + h);  // wave-uniform
-          const float boff = m > 0 ? exp2f(static_cast<float>(16 * m + lane_off) * lg) : 0.0f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float f;
-            if (m > 0) f = boff * cst[e];
-            else if (m == 0) f = Ddg[e];
-            else f = 0.0f;
-            p[4 * h + e] = (h == 0 ? St[qi][0][e] : (need1[qi] ? St[qi][1][e] : 0.0f)) * f;
-          }
-        }
-        const bf16x8 pa = __builtin_convertvector(p, bf16x8);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) O[qi][nb] = mfma(pa, vb[nb], O[qi][nb]);
-      }
-    }
-    // Q of the next chunk: issued before this chunk's Y stores so that the
-    // next phase A waits on these loads only, not on the stores
-    load_q(s1, Ln);
-    // store Y rows (rows past the chunk end fall outside the buffer and are dropped)
-    {
-      const rsrc_t ry = make_rsrc(yh + static_cast<long>(s0) * dv, static_cast<uint32_t>(L - 1) * vrow + kTN * 2u);
-#pragma unroll
-      for (int qi = 0; qi < F::NQ; ++qi)
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t roff = static_cast<uint32_t>(16 * qblk[qi] + 4 * g + i) * vrow + 2u * c16;
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb) buffer_store2(ry, roff + 32u * nb, f32_to_bf16(O[qi][nb][i]));
+          const int d = dbase + 16 * mb + 4 * g + i;
+          Racc[mb][nb][i] = state_in != nullptr ? state_in[sbase + static_cast<long>(d) * dv + 16 * nb + c16] : 0.0f;
         }
-    }
-    __syncthreads();  // all waves are done reading R^T, V and K for outputs
+    auto write_rt = [&]() {
+#pragma unroll
+      for (int mb = 0; mb < F::RM; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const bf16x4 r = __builtin_convertvector(Racc[mb][nb], bf16x4);
+          *reinterpret_cast<bf16x4*>(&Rt[(16 * nb + c16) * F::RLD + dbase + 16 * mb + 4 * g]) = r;
+        }
+    };
+    // Staging map: groups of 8 lanes read 128 contiguous bytes per instruction;
+    // a thread's pieces are 128 bytes (K) or one row (V) apart, so the
+    // per-piece offsets fit the instructions' immediate offset field.
+    u32x4 kreg[F::KPT];
+    u32x4 vreg[F::VPT];
+    const int grp = st >> 3, gl = st & 7;
+    const uint32_t koff = static_cast<uint32_t>(grp * 8 * F::KPT + gl) * 16u;  // + 128 r
+    const int vrow0 = grp * F::VPT;                                            // rows vrow0 + r
+    const uint32_t voff = static_cast<uint32_t>(vrow0) * vrow + 16u * gl;      // + r * vrow
+    float zfull[F::VPT];  // gamma^(C-1-row) for full chunks
+#pragma unroll
+    for (int r = 0; r < F::VPT; ++r) zfull[r] = vrow0 + r < C ? gamma_pow(lg, C - 1 - (vrow0 + r)) : 0.0f;
+    auto load_kv = [&](int s1, int Ln) {
+      const rsrc_t rk = make_rsrc(kh + static_cast<long>(s1) * DK, static_cast<uint32_t>(Ln) * DK * 2u);
+#pragma unroll
+      for (int r = 0; r < F::KPT; ++r) kreg[r] = buffer_load16(rk, koff + 128u * r);
+      const rsrc_t rv = make_rsrc(vh + static_cast<long>(s1) * dv,
+                                  Ln > 0 ? static_cast<uint32_t>(Ln - 1) * vrow + kTN * 2u : 0u);
+#pragma unroll
+      for (int r = 0; r < F::VPT; ++r) vreg[r] = buffer_load16(rv, voff + vrow * r);
+    };
+    auto store_kv = [&](int Ln) {
+#pragma unroll
+      for (int r = 0; r < F::KPT; ++r) {
+        const int p = grp * 8 * F::KPT + 8 * r + gl;
+        const int row = p / (DK / 8), c8 = p % (DK / 8);
+        *reinterpret_cast<u32x4*>(&Ks[row * F::KLD + 8 * c8]) = kreg[r];
+      }
+#pragma unroll
+      for (int r = 0; r < F::VPT; ++r) {
+        const int row = vrow0 + r;
+        *reinterpret_cast<u32x4*>(&Vs[row * F::VLD + 8 * gl]) = vreg[r];
+        // zeta_row = gamma^(L-1-row) scales V for the state update (0 past the chunk end)
+        const float z = Ln == C ? zfull[r] : (row < Ln ? gamma_pow(lg, Ln - 1 - row) : 0.0f);
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, vreg[r]);
+        const f32x8 vf = __builtin_convertvector(vb, f32x8) * z;
+        *reinterpret_cast<bf16x8*>(&Vz[row * F::VLD + 8 * gl]) = __builtin_convertvector(vf, bf16x8);
+      }
+    };
 
-    // ================= phase B: state update =================
     {
+      const int L0 = min(C, Tn);
+      load_kv(0, L0);
+      write_rt();
+      store_kv(L0);
+    }
+    __syncthreads();  // chunk 0 staged, R_0 published
+
+    for (int ci = 0; ci < nchunks; ++ci) {
+      const int s0 = ci * C;
+      const int L = min(C, Tn - s0);
+      const int s1 = s0 + C;
+      const int Ln = s1 < Tn ? min(C, Tn - s1) : 0;
+      // next chunk's K/V, issued unconditionally (an empty buffer past the end
+      // reads zeros) so the wait counts stay exact; consumed after the barrier
+      load_kv(s1, Ln);
+
+      // R <- gamma^L R + K^T (zeta V).  The token contraction uses k-slot e of
+      // lane group g <-> token 32s + 8g + 2(e%4) + e/4 for both operands: each
+      // transposing read then touches rows {0,2,..,14} or {1,3,..,15} (+16),
+      // which the padded row strides place in disjoint LDS banks.
       const float gL = L == C ? gamma_pow(lg, C) : gamma_pow(lg, L);
 #pragma unroll
       for (int mb = 0; mb < F::RM; ++mb)
@@ -367,69 +231,206 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
       for (int s = 0; s < CT / 32; ++s) {
         if (32 * s >= L) break;
-        bf16x8 zb[4];
+        bf16x8 zb[4], ka[F::RM];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
           const int col = 16 * nb + 4 * (c16 & 3);
-          const s16x4 lo = lds_read_tr(&Vz[(32 * s + 8 * g + (c16 >> 2)) * F::VLD + col]);
-          const s16x4 hi = lds_read_tr(&Vz[(32 * s + 8 * g + 4 + (c16 >> 2)) * F::VLD + col]);
+          const s16x4 lo = lds_read_tr(&Vz[(32 * s + 8 * g + 2 * (c16 >> 2)) * F::VLD + col]);
+          const s16x4 hi = lds_read_tr(&Vz[(32 * s + 8 * g + 2 * (c16 >> 2) + 1) * F::VLD + col]);
           zb[nb] = join(lo, hi);
         }
 #pragma unroll
         for (int mb = 0; mb < F::RM; ++mb) {
           const int col = dbase + 16 * mb + 4 * (c16 & 3);
-          const s16x4 lo = lds_read_tr(&Ks[(32 * s + 8 * g + (c16 >> 2)) * F::KLD + col]);
-          const s16x4 hi = lds_read_tr(&Ks[(32 * s + 8 * g + 4 + (c16 >> 2)) * F::KLD + col]);
-          const bf16x8 ka = join(lo, hi);
+          const s16x4 lo = lds_read_tr(&Ks[(32 * s + 8 * g + 2 * (c16 >> 2)) * F::KLD + col]);
+          const s16x4 hi = lds_read_tr(&Ks[(32 * s + 8 * g + 2 * (c16 >> 2) + 1) * F::KLD + col]);
+          ka[mb] = join(lo, hi);
+        }
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) Racc[mb][nb] = mfma(ka, zb[nb], Racc[mb][nb]);
+        for (int mb = 0; mb < F::RM; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) Racc[mb][nb] = mfma(ka[mb], zb[nb], Racc[mb][nb]);
+      }
+      __syncthreads();  // output waves are done with R^T, K and V of this chunk
+      write_rt();
+      if (Ln > 0) store_kv(Ln);
+      __syncthreads();  // R_(i+1) and the next chunk's K/V are in LDS
+    }
+
+    if (state_out != nullptr) {
+#pragma unroll
+      for (int mb = 0; mb < F::RM; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d = dbase + 16 * mb + 4 * g + i;
+            state_out[sbase + static_cast<long>(d) * dv + 16 * nb + c16] = Racc[mb][nb][i];
+          }
+    }
+  } else {
+    // =========================== output waves ===========================
+    int qblk[F::NQ];
+    if constexpr (F::NQ == 2) {
+      qblk[0] = wr;
+      qblk[1] = 7 - wr;
+    } else {
+      qblk[0] = wr;
+    }
+    // Decay factors (positions are chunk-relative, so these do not depend on
+    // the chunk).  Off-diagonal key block kb < qb:
+    //   gamma^(j-t) = gamma^(16(qb-kb) + c16 - 4g - 3) * cst[t % 4],  cst[e] = gamma^(3-e)
+    // (both exponents >= 0: no overflow for any gamma in [0,1]); diagonal key
+    // block: Ddg[e] = gamma^(c16 - 4g - e) on or below the diagonal, else 0.
+    float cst[4], Ddg[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      cst[e] = gamma_pow(lg, 3 - e);
+      const int d = c16 - 4 * g - e;
+      Ddg[e] = d >= 0 ? gamma_pow(lg, d) : 0.0f;
+    }
+    const int lane_off = c16 - 4 * g - 3;
+    bf16x8 Qreg[F::NQ][F::KS];
+    auto load_q = [&](int s1, int Ln) {
+      const rsrc_t rq = make_rsrc(qh + static_cast<long>(s1) * DK, static_cast<uint32_t>(Ln) * DK * 2u);
+#pragma unroll
+      for (int qi = 0; qi < F::NQ; ++qi) {
+        const uint32_t rowoff = static_cast<uint32_t>(16 * qblk[qi] + c16) * DK * 2u + 16u * g;
+#pragma unroll
+        for (int s = 0; s < F::KS; ++s) Qreg[qi][s] = __builtin_bit_cast(bf16x8, buffer_load16(rq, rowoff + 64u * s));
+      }
+    };
+    load_q(0, min(C, Tn));
+    __syncthreads();  // chunk 0 staged, R_0 published
+
+    for (int ci = 0; ci < nchunks; ++ci) {
+      const int s0 = ci * C;
+      const int L = min(C, Tn - s0);
+      const int s1 = s0 + C;
+      const int Ln = s1 < Tn ? min(C, Tn - s1) : 0;
+
+      // cross-chunk term first: O = gamma^(j+1) (Q R_i), then P V accumulates on top
+      f32x4 O[F::NQ][4];
+      {
+        bf16x8 rb[2][4];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) rb[0][nb] = lds_read16(&Rt[(16 * nb + c16) * F::RLD + 8 * g]);
+#pragma unroll
+        for (int s = 0; s < F::KS; ++s) {
+          if (s + 1 < F::KS) {
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+              rb[(s + 1) & 1][nb] = lds_read16(&Rt[(16 * nb + c16) * F::RLD + 32 * (s + 1) + 8 * g]);
+          }
+#pragma unroll
+          for (int qi = 0; qi < F::NQ; ++qi)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+              O[qi][nb] = mfma(Qreg[qi][s], rb[s & 1][nb], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : O[qi][nb]);
         }
       }
-      write_rt();
-    }
-    __syncthreads();  // K and zeta*V fully consumed; R^T rewritten
-    if (has_next) {
-      store_kv(Ln);
-      __syncthreads();
-    }
-  }
-
-  if (state_out != nullptr) {
 #pragma unroll
-    for (int mb = 0; mb < F::RM; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int qi = 0; qi < F::NQ; ++qi)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int d = dbase + 16 * mb + 4 * g + i;
-          state_out[sbase + static_cast<long>(d) * dv + 16 * nb + c16] = Racc[mb][nb][i];
+          const float xi = gamma_pow(lg, 16 * qblk[qi] + 4 * g + i + 1);
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) O[qi][nb][i] *= xi;
         }
+
+      // intra-chunk term: key steps of 32 keys on or below the diagonal
+      const int qmax = F::NQ == 2 ? max(qblk[0], qblk[1]) : qblk[0];
+      f32x4 St[F::NQ][NSP][2];
+#pragma unroll
+      for (int sp = 0; sp < NSP; ++sp) {
+        if (2 * sp > qmax) break;
+#pragma unroll
+        for (int s = 0; s < F::KS; ++s) {
+          const bf16x8 ka = lds_read16(&Ks[(32 * sp + c16) * F::KLD + 32 * s + 8 * g]);
+          const bf16x8 kb = lds_read16(&Ks[(32 * sp + 16 + c16) * F::KLD + 32 * s + 8 * g]);
+#pragma unroll
+          for (int qi = 0; qi < F::NQ; ++qi) {
+            if (qblk[qi] >= 2 * sp)
+              St[qi][sp][0] = mfma(ka, Qreg[qi][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : St[qi][sp][0]);
+            if (qblk[qi] >= 2 * sp + 1)
+              St[qi][sp][1] = mfma(kb, Qreg[qi][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : St[qi][sp][1]);
+          }
+        }
+      }
+      // Q of the next chunk: the operand registers are free now
+      load_q(s1, Ln);
+#pragma unroll
+      for (int sp = 0; sp < NSP; ++sp) {
+        if (2 * sp > qmax) break;
+        // V operands (keys 32sp+4g+e and 32sp+16+4g+e), shared by the wave's query blocks
+        bf16x8 vb[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int col = 16 * nb + 4 * (c16 & 3);
+          const s16x4 lo = lds_read_tr(&Vs[(32 * sp + 4 * g + (c16 >> 2)) * F::VLD + col]);
+          const s16x4 hi = lds_read_tr(&Vs[(32 * sp + 16 + 4 * g + (c16 >> 2)) * F::VLD + col]);
+          vb[nb] = join(lo, hi);
+        }
+#pragma unroll
+        for (int qi = 0; qi < F::NQ; ++qi) {
+          if (qblk[qi] < 2 * sp) continue;
+          f32x8 p;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int m = qblk[qi] - (2 * sp + h);  // wave-uniform
+            const float boff = m > 0 ? exp2f(static_cast<float>(16 * m + lane_off) * lg) : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float f;
+              if (m > 0) f = boff * cst[e];
+              else if (m == 0) f = Ddg[e];
+              else f = 0.0f;
+              p[4 * h + e] = m >= 0 ? St[qi][sp][h][e] * f : 0.0f;
+            }
+          }
+          const bf16x8 pa = __builtin_convertvector(p, bf16x8);
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) O[qi][nb] = mfma(pa, vb[nb], O[qi][nb]);
+        }
+      }
+      __syncthreads();  // this chunk's K, V and R^T are no longer read
+      // store Y rows (rows past the chunk end fall outside the buffer and are dropped)
+      {
+        const rsrc_t ry = make_rsrc(yh + static_cast<long>(s0) * dv, static_cast<uint32_t>(L - 1) * vrow + kTN * 2u);
+#pragma unroll
+        for (int qi = 0; qi < F::NQ; ++qi)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t roff = static_cast<uint32_t>(16 * qblk[qi] + 4 * g + i) * vrow + 2u * c16;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) buffer_store2(ry, roff + 32u * nb, f32_to_bf16(O[qi][nb][i]));
+          }
+      }
+      __syncthreads();  // R_(i+1) and the next chunk's K/V are in LDS
+    }
   }
 }
 
-template <int CT, int DK, int NW>
+template <int CT, int DK>
 hipError_t launch_cfg(const void* q, const void* k, const void* v, const float* state_in, float* state_out, void* y,
                       int B, int H, int Tn, int dv, int C, const HeadDecay& hd, const HeadGroup& g, hipStream_t s) {
   const int ntiles = dv / kTN;
   const int total = B * g.nh * ntiles;
-  hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, NW>), dim3(total), dim3(64 * NW), 0, s,
+  hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK>), dim3(total), dim3(Cfg<CT, DK>::kThreads), 0, s,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), state_in, state_out, static_cast<uint16_t*>(y), hd, H, g.h0,
                      g.nh, Tn, dv, C, ntiles);
   return hipGetLastError();
 }
 
-// 64-token tiles run 4 waves (one query block each); 128-token tiles run 8
-// waves (two per SIMD) when d_k allows 32 state rows per wave.
 template <int CT>
 hipError_t launch_ct(const void* q, const void* k, const void* v, const float* state_in, float* state_out, void* y,
                      int B, int H, int Tn, int dk, int dv, int C, const HeadDecay& hd, const HeadGroup& g,
                      hipStream_t s) {
-  constexpr int NW = CT == 128 ? 8 : 4;
   switch (dk) {
-    case 64: return launch_cfg<CT, 64, 4>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, s);
-    case 128: return launch_cfg<CT, 128, NW>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, s);
-    default: return launch_cfg<CT, 256, NW>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, s);
+    case 64: return launch_cfg<CT, 64>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, s);
+    case 128: return launch_cfg<CT, 128>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, s);
+    default: return launch_cfg<CT, 256>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, s);
   }
 }
 
