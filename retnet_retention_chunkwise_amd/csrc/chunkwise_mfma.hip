@@ -24,10 +24,14 @@
 //     transposing LDS load.  The cross term reads R^T (bf16) from LDS.
 //   * state waves 4..7 own d_k/4 rows of the fp32 state tile R[d_k x 64],
 //     kept in MFMA accumulators for the whole sequence.  They run the update
-//     R <- gamma^L R + K^T (zeta V) (K^T and zeta V through the transposing
-//     load), publish R^T to LDS, and stage the next chunk's K and V tiles
-//     (global loads into registers during the chunk, LDS writes after it).
-// Per chunk: [outputs | update] barrier [R^T and next K/V written] barrier.
+//     R <- gamma^L R + K^T (zeta V) (K^T and V through the transposing load,
+//     zeta_j = gamma^(L-1-j) applied in registers), publish R^T to LDS, and
+//     stage the next chunk's K and V tiles (global loads into registers a
+//     chunk ahead, LDS writes after the update).
+// 64-token chunks keep two copies of K, V and R^T in LDS, so staging chunk
+// i+1 overlaps the outputs of chunk i and one barrier per chunk suffices;
+// 128-token chunks keep one copy: [outputs | update] barrier [R^T and next
+// K/V written] barrier.
 // Every global access goes through a buffer resource that ends at the
 // chunk's last valid row, so rows past the end read as zero / are dropped
 // without branches.  Decay factors gamma^d come from log2(gamma) with
@@ -86,13 +90,17 @@ struct Cfg {
   static constexpr int kThreads = 512;         // 4 output waves + 4 state waves
   static constexpr int kStageThreads = 256;    // the state waves stage K/V
   static constexpr int KLD = DK + 8;           // K row stride in LDS (elements)
-  static constexpr int VLD = kTN + 8;          // V / zeta*V row stride
+  static constexpr int VLD = kTN + 8;          // V row stride
   static constexpr int RLD = DK + 8;           // R^T row stride
   static constexpr int NQ = CT / 64;           // query blocks per output wave
   static constexpr int RM = DK / 64;           // 16-row state blocks per state wave
   static constexpr int KS = DK / 32;           // k-steps over d_k
   static constexpr int KPT = CT * DK / 8 / kStageThreads;   // 16-byte K pieces per staging thread
   static constexpr int VPT = CT * kTN / 8 / kStageThreads;  // 16-byte V pieces per staging thread
+  // 64-token tiles fit two copies of K, V and R^T in LDS: the state waves then
+  // stage chunk i+1 while the output waves work on chunk i (one barrier per
+  // chunk).  128-token tiles keep one copy and two barriers per chunk.
+  static constexpr int NBUF = (2 * (CT * KLD + CT * VLD + kTN * RLD) * 2 <= 160 * 1024) ? 2 : 1;
   static_assert(NQ >= 1 && NQ <= 2 && RM >= 1, "unsupported tile");
   static_assert(KPT >= 1 && VPT >= 1, "tile too small for the staging split");
 };
@@ -104,11 +112,15 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                       uint16_t* __restrict__ y, HeadDecay gam, int H, int h0, int nh, int Tn, int dv, int C,
                       int ntiles) {
   using F = Cfg<CT, DK>;
-  constexpr int NSP = CT / 32;  // key steps of 32 keys per chunk tile
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[CT * F::KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[CT * F::VLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vz[CT * F::VLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Rt[kTN * F::RLD];
+  constexpr int NSP = CT / 32;  // key (token) steps of 32 per chunk tile
+  constexpr int NB = F::NBUF;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[NB][CT * F::KLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[NB][CT * F::VLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Rt[NB][kTN * F::RLD];
+  // With one LDS copy there is room for zeta*V, formed once when V is staged;
+  // with two copies zeta is applied to the update's V operand in registers.
+  constexpr bool kVz = NB == 1;
+  __shared__ __attribute__((aligned(16))) uint16_t Vz[kVz ? CT * F::VLD : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -153,13 +165,13 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
           const int d = dbase + 16 * mb + 4 * g + i;
           Racc[mb][nb][i] = state_in != nullptr ? state_in[sbase + static_cast<long>(d) * dv + 16 * nb + c16] : 0.0f;
         }
-    auto write_rt = [&]() {
+    auto write_rt = [&](int buf) {
 #pragma unroll
       for (int mb = 0; mb < F::RM; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
           const bf16x4 r = __builtin_convertvector(Racc[mb][nb], bf16x4);
-          *reinterpret_cast<bf16x4*>(&Rt[(16 * nb + c16) * F::RLD + dbase + 16 * mb + 4 * g]) = r;
+          *reinterpret_cast<bf16x4*>(&Rt[buf][(16 * nb + c16) * F::RLD + dbase + 16 * mb + 4 * g]) = r;
         }
     };
     // Staging map: groups of 8 lanes read 128 contiguous bytes per instruction;
@@ -171,9 +183,6 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     const uint32_t koff = static_cast<uint32_t>(grp * 8 * F::KPT + gl) * 16u;  // + 128 r
     const int vrow0 = grp * F::VPT;                                            // rows vrow0 + r
     const uint32_t voff = static_cast<uint32_t>(vrow0) * vrow + 16u * gl;      // + r * vrow
-    float zfull[F::VPT];  // gamma^(C-1-row) for full chunks
-#pragma unroll
-    for (int r = 0; r < F::VPT; ++r) zfull[r] = vrow0 + r < C ? gamma_pow(lg, C - 1 - (vrow0 + r)) : 0.0f;
     auto load_kv = [&](int s1, int Ln) {
       const rsrc_t rk = make_rsrc(kh + static_cast<long>(s1) * DK, static_cast<uint32_t>(Ln) * DK * 2u);
 #pragma unroll
@@ -183,30 +192,113 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
       for (int r = 0; r < F::VPT; ++r) vreg[r] = buffer_load16(rv, voff + vrow * r);
     };
-    auto store_kv = [&](int Ln) {
+    auto store_kv = [&](int buf) {
 #pragma unroll
       for (int r = 0; r < F::KPT; ++r) {
         const int p = grp * 8 * F::KPT + 8 * r + gl;
         const int row = p / (DK / 8), c8 = p % (DK / 8);
-        *reinterpret_cast<u32x4*>(&Ks[row * F::KLD + 8 * c8]) = kreg[r];
+        *reinterpret_cast<u32x4*>(&Ks[buf][row * F::KLD + 8 * c8]) = kreg[r];
       }
+#pragma unroll
+      for (int r = 0; r < F::VPT; ++r) *reinterpret_cast<u32x4*>(&Vs[buf][(vrow0 + r) * F::VLD + 8 * gl]) = vreg[r];
+    };
+    // zeta*V for the one-copy layout: zeta_row = gamma^(L-1-row), 0 past the chunk end
+    auto store_vz = [&](int Ln) {
 #pragma unroll
       for (int r = 0; r < F::VPT; ++r) {
         const int row = vrow0 + r;
-        *reinterpret_cast<u32x4*>(&Vs[row * F::VLD + 8 * gl]) = vreg[r];
-        // zeta_row = gamma^(L-1-row) scales V for the state update (0 past the chunk end)
-        const float z = Ln == C ? zfull[r] : (row < Ln ? gamma_pow(lg, Ln - 1 - row) : 0.0f);
-        const bf16x8 vb = __builtin_bit_cast(bf16x8, vreg[r]);
-        const f32x8 vf = __builtin_convertvector(vb, f32x8) * z;
+        const float z = row < Ln ? gamma_pow(lg, Ln - 1 - row) : 0.0f;
+        const f32x8 vf = __builtin_convertvector(__builtin_bit_cast(bf16x8, vreg[r]), f32x8) * z;
         *reinterpret_cast<bf16x8*>(&Vz[row * F::VLD + 8 * gl]) = __builtin_convertvector(vf, bf16x8);
+      }
+    };
+    // zeta_t = gamma^(L-1-t) for the tokens t = 32s + 8g + 2(e%4) + e/4 this lane
+    // holds in the update's B operand; for chunks that fill the tile (L = CT),
+    // zeta = zbase[s] * zc[e] with zbase[s] = gamma^(CT-8-32s-8g) and
+    // zc[e] = gamma^(7-2(e%4)-e/4) (both exponents >= 0).
+    float zbase[NSP], zc[8];
+#pragma unroll
+    for (int s = 0; s < NSP; ++s) zbase[s] = gamma_pow(lg, CT - 8 - 32 * s - 8 * g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zc[e] = gamma_pow(lg, 7 - 2 * (e & 3) - (e >> 2));
+
+    // R <- gamma^L R + K^T (zeta V) on LDS buffer `buf`.  The token contraction
+    // uses k-slot e of lane group g <-> token 32s + 8g + 2(e%4) + e/4 for both
+    // operands: each transposing read then touches rows {0,2,..,14} or
+    // {1,3,..,15} (+16), which the padded row strides place in disjoint banks.
+    auto update = [&](int buf, int L) {
+      const float gL = L == C ? gamma_pow(lg, C) : gamma_pow(lg, L);
+#pragma unroll
+      for (int mb = 0; mb < F::RM; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) Racc[mb][nb] *= gL;
+      // With two LDS copies (64-token tiles) the operands of step s+1 are read
+      // before the MFMAs of step s; 128-token tiles hold the K/V staging
+      // registers of a full tile and read each step just before use.
+      constexpr int PB = NB == 2 ? 2 : 1;
+      bf16x8 zb[PB][4], ka[PB][F::RM];
+      auto read_step = [&](int s, int slot) {
+        const uint16_t* vsrc = kVz ? Vz : Vs[buf];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int col = 16 * nb + 4 * (c16 & 3);
+          const s16x4 lo = lds_read_tr(&vsrc[(32 * s + 8 * g + 2 * (c16 >> 2)) * F::VLD + col]);
+          const s16x4 hi = lds_read_tr(&vsrc[(32 * s + 8 * g + 2 * (c16 >> 2) + 1) * F::VLD + col]);
+          zb[slot][nb] = join(lo, hi);
+        }
+#pragma unroll
+        for (int mb = 0; mb < F::RM; ++mb) {
+          const int col = dbase + 16 * mb + 4 * (c16 & 3);
+          const s16x4 lo = lds_read_tr(&Ks[buf][(32 * s + 8 * g + 2 * (c16 >> 2)) * F::KLD + col]);
+          const s16x4 hi = lds_read_tr(&Ks[buf][(32 * s + 8 * g + 2 * (c16 >> 2) + 1) * F::KLD + col]);
+          ka[slot][mb] = join(lo, hi);
+        }
+      };
+      if constexpr (PB == 2) read_step(0, 0);
+#pragma unroll
+      for (int s = 0; s < NSP; ++s) {
+        if (32 * s >= L) break;
+        const int slot = PB == 2 ? (s & 1) : 0;
+        if constexpr (PB == 2) {
+          if (s + 1 < NSP && 32 * (s + 1) < L) read_step(s + 1, (s + 1) & 1);
+        } else {
+          read_step(s, 0);
+        }
+        // zeta-scale the V operand of step s (in place)
+        if constexpr (!kVz) {
+        float z[8];
+        if (L == CT) {  // a full tile: every token group lies inside the chunk
+#pragma unroll
+          for (int e = 0; e < 8; ++e) z[e] = zbase[s] * zc[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int t = 32 * s + 8 * g + 2 * (e & 3) + (e >> 2);
+            z[e] = t < L ? gamma_pow(lg, L - 1 - t) : 0.0f;
+          }
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          f32x8 vf = __builtin_convertvector(zb[slot][nb], f32x8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vf[e] *= z[e];
+          zb[slot][nb] = __builtin_convertvector(vf, bf16x8);
+        }
+        }
+#pragma unroll
+        for (int mb = 0; mb < F::RM; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) Racc[mb][nb] = mfma(ka[slot][mb], zb[slot][nb], Racc[mb][nb]);
       }
     };
 
     {
       const int L0 = min(C, Tn);
       load_kv(0, L0);
-      write_rt();
-      store_kv(L0);
+      write_rt(0);
+      store_kv(0);
+      if constexpr (kVz) store_vz(L0);
+      if constexpr (NB == 2) load_kv(C, C < Tn ? min(C, Tn - C) : 0);  // chunk 1 into registers
     }
     __syncthreads();  // chunk 0 staged, R_0 published
 
@@ -215,46 +307,27 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       const int L = min(C, Tn - s0);
       const int s1 = s0 + C;
       const int Ln = s1 < Tn ? min(C, Tn - s1) : 0;
-      // next chunk's K/V, issued unconditionally (an empty buffer past the end
-      // reads zeros) so the wait counts stay exact; consumed after the barrier
-      load_kv(s1, Ln);
-
-      // R <- gamma^L R + K^T (zeta V).  The token contraction uses k-slot e of
-      // lane group g <-> token 32s + 8g + 2(e%4) + e/4 for both operands: each
-      // transposing read then touches rows {0,2,..,14} or {1,3,..,15} (+16),
-      // which the padded row strides place in disjoint LDS banks.
-      const float gL = L == C ? gamma_pow(lg, C) : gamma_pow(lg, L);
-#pragma unroll
-      for (int mb = 0; mb < F::RM; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) Racc[mb][nb] *= gL;
-#pragma unroll
-      for (int s = 0; s < CT / 32; ++s) {
-        if (32 * s >= L) break;
-        bf16x8 zb[4], ka[F::RM];
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int col = 16 * nb + 4 * (c16 & 3);
-          const s16x4 lo = lds_read_tr(&Vz[(32 * s + 8 * g + 2 * (c16 >> 2)) * F::VLD + col]);
-          const s16x4 hi = lds_read_tr(&Vz[(32 * s + 8 * g + 2 * (c16 >> 2) + 1) * F::VLD + col]);
-          zb[nb] = join(lo, hi);
+      if constexpr (NB == 2) {
+        const int X = ci & 1;
+        update(X, L);
+        write_rt(X ^ 1);                 // R_(i+1) into the other copy
+        if (Ln > 0) store_kv(X ^ 1);     // chunk i+1 (loaded during chunk i-1)
+        const int s2 = s1 + C;
+        load_kv(s2, s2 < Tn ? min(C, Tn - s2) : 0);  // chunk i+2 into registers
+        __syncthreads();
+      } else {
+        // next chunk's K/V, issued unconditionally (an empty buffer past the end
+        // reads zeros) so the wait counts stay exact; written after the barrier
+        load_kv(s1, Ln);
+        update(0, L);
+        __syncthreads();  // output waves are done with R^T, K and V of this chunk
+        write_rt(0);
+        if (Ln > 0) {
+          store_kv(0);
+          store_vz(Ln);
         }
-#pragma unroll
-        for (int mb = 0; mb < F::RM; ++mb) {
-          const int col = dbase + 16 * mb + 4 * (c16 & 3);
-          const s16x4 lo = lds_read_tr(&Ks[(32 * s + 8 * g + 2 * (c16 >> 2)) * F::KLD + col]);
-          const s16x4 hi = lds_read_tr(&Ks[(32 * s + 8 * g + 2 * (c16 >> 2) + 1) * F::KLD + col]);
-          ka[mb] = join(lo, hi);
-        }
-#pragma unroll
-        for (int mb = 0; mb < F::RM; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb) Racc[mb][nb] = mfma(ka[mb], zb[nb], Racc[mb][nb]);
+        __syncthreads();  // R_(i+1) and the next chunk's K/V are in LDS
       }
-      __syncthreads();  // output waves are done with R^T, K and V of this chunk
-      write_rt();
-      if (Ln > 0) store_kv(Ln);
-      __syncthreads();  // R_(i+1) and the next chunk's K/V are in LDS
     }
 
     if (state_out != nullptr) {
@@ -308,19 +381,23 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       const int L = min(C, Tn - s0);
       const int s1 = s0 + C;
       const int Ln = s1 < Tn ? min(C, Tn - s1) : 0;
+      const int X = NB == 2 ? (ci & 1) : 0;
+      const uint16_t* Kx = Ks[X];
+      const uint16_t* Vx = Vs[X];
+      const uint16_t* Rx = Rt[X];
 
       // cross-chunk term first: O = gamma^(j+1) (Q R_i), then P V accumulates on top
       f32x4 O[F::NQ][4];
       {
         bf16x8 rb[2][4];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) rb[0][nb] = lds_read16(&Rt[(16 * nb + c16) * F::RLD + 8 * g]);
+        for (int nb = 0; nb < 4; ++nb) rb[0][nb] = lds_read16(&Rx[(16 * nb + c16) * F::RLD + 8 * g]);
 #pragma unroll
         for (int s = 0; s < F::KS; ++s) {
           if (s + 1 < F::KS) {
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
-              rb[(s + 1) & 1][nb] = lds_read16(&Rt[(16 * nb + c16) * F::RLD + 32 * (s + 1) + 8 * g]);
+              rb[(s + 1) & 1][nb] = lds_read16(&Rx[(16 * nb + c16) * F::RLD + 32 * (s + 1) + 8 * g]);
           }
 #pragma unroll
           for (int qi = 0; qi < F::NQ; ++qi)
@@ -338,37 +415,39 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
           for (int nb = 0; nb < 4; ++nb) O[qi][nb][i] *= xi;
         }
 
-      // intra-chunk term: key steps of 32 keys on or below the diagonal
+      // intra-chunk term: key steps of 32 keys on or below the diagonal.  When
+      // the scores of all key steps fit in registers (64-token tiles), every
+      // S^T block is computed first so that the next chunk's Q loads can be
+      // issued before the P V products; otherwise S^T and P V alternate per
+      // key step and the Q loads follow.
       const int qmax = F::NQ == 2 ? max(qblk[0], qblk[1]) : qblk[0];
-      f32x4 St[F::NQ][NSP][2];
-#pragma unroll
-      for (int sp = 0; sp < NSP; ++sp) {
-        if (2 * sp > qmax) break;
+      constexpr bool kAllScoresFirst = true;
+      constexpr int NSS = kAllScoresFirst ? NSP : 1;  // key steps whose scores are live at once
+      f32x4 St[F::NQ][NSS][2];
+      auto scores = [&](int sp) {
+        const int slot = kAllScoresFirst ? sp : 0;
 #pragma unroll
         for (int s = 0; s < F::KS; ++s) {
-          const bf16x8 ka = lds_read16(&Ks[(32 * sp + c16) * F::KLD + 32 * s + 8 * g]);
-          const bf16x8 kb = lds_read16(&Ks[(32 * sp + 16 + c16) * F::KLD + 32 * s + 8 * g]);
+          const bf16x8 ka = lds_read16(&Kx[(32 * sp + c16) * F::KLD + 32 * s + 8 * g]);
+          const bf16x8 kb = lds_read16(&Kx[(32 * sp + 16 + c16) * F::KLD + 32 * s + 8 * g]);
 #pragma unroll
           for (int qi = 0; qi < F::NQ; ++qi) {
             if (qblk[qi] >= 2 * sp)
-              St[qi][sp][0] = mfma(ka, Qreg[qi][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : St[qi][sp][0]);
+              St[qi][slot][0] = mfma(ka, Qreg[qi][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : St[qi][slot][0]);
             if (qblk[qi] >= 2 * sp + 1)
-              St[qi][sp][1] = mfma(kb, Qreg[qi][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : St[qi][sp][1]);
+              St[qi][slot][1] = mfma(kb, Qreg[qi][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : St[qi][slot][1]);
           }
         }
-      }
-      // Q of the next chunk: the operand registers are free now
-      load_q(s1, Ln);
-#pragma unroll
-      for (int sp = 0; sp < NSP; ++sp) {
-        if (2 * sp > qmax) break;
+      };
+      auto pv = [&](int sp) {
+        const int slot = kAllScoresFirst ? sp : 0;
         // V operands (keys 32sp+4g+e and 32sp+16+4g+e), shared by the wave's query blocks
         bf16x8 vb[4];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
           const int col = 16 * nb + 4 * (c16 & 3);
-          const s16x4 lo = lds_read_tr(&Vs[(32 * sp + 4 * g + (c16 >> 2)) * F::VLD + col]);
-          const s16x4 hi = lds_read_tr(&Vs[(32 * sp + 16 + 4 * g + (c16 >> 2)) * F::VLD + col]);
+          const s16x4 lo = lds_read_tr(&Vx[(32 * sp + 4 * g + (c16 >> 2)) * F::VLD + col]);
+          const s16x4 hi = lds_read_tr(&Vx[(32 * sp + 16 + 4 * g + (c16 >> 2)) * F::VLD + col]);
           vb[nb] = join(lo, hi);
         }
 #pragma unroll
@@ -385,15 +464,32 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
               if (m > 0) f = boff * cst[e];
               else if (m == 0) f = Ddg[e];
               else f = 0.0f;
-              p[4 * h + e] = m >= 0 ? St[qi][sp][h][e] * f : 0.0f;
+              p[4 * h + e] = m >= 0 ? St[qi][slot][h][e] * f : 0.0f;
             }
           }
           const bf16x8 pa = __builtin_convertvector(p, bf16x8);
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb) O[qi][nb] = mfma(pa, vb[nb], O[qi][nb]);
         }
+      };
+      if constexpr (kAllScoresFirst) {
+#pragma unroll
+        for (int sp = 0; sp < NSP; ++sp)
+          if (2 * sp <= qmax) scores(sp);
+        load_q(s1, Ln);  // the Q operand registers are free now
+#pragma unroll
+        for (int sp = 0; sp < NSP; ++sp)
+          if (2 * sp <= qmax) pv(sp);
+      } else {
+#pragma unroll
+        for (int sp = 0; sp < NSP; ++sp) {
+          if (2 * sp > qmax) break;
+          scores(sp);
+          pv(sp);
+        }
+        load_q(s1, Ln);
       }
-      __syncthreads();  // this chunk's K, V and R^T are no longer read
+      if constexpr (NB == 1) __syncthreads();  // this chunk's K, V and R^T are no longer read
       // store Y rows (rows past the chunk end fall outside the buffer and are dropped)
       {
         const rsrc_t ry = make_rsrc(yh + static_cast<long>(s0) * dv, static_cast<uint32_t>(L - 1) * vrow + kTN * 2u);
@@ -406,7 +502,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
             for (int nb = 0; nb < 4; ++nb) buffer_store2(ry, roff + 32u * nb, f32_to_bf16(O[qi][nb][i]));
           }
       }
-      __syncthreads();  // R_(i+1) and the next chunk's K/V are in LDS
+      __syncthreads();  // the next chunk's R^T, K and V are in LDS
     }
   }
 }

@@ -8,7 +8,9 @@
 //   - one workgroup (4 waves) per (batch, head, slice of 64*VEC columns);
 //   - lane l of every wave owns VEC consecutive columns, so each wave moves
 //     64*VEC*4 contiguous bytes per state row (dwordx4 accesses for VEC = 4);
-//   - the 4 waves take interleaved rows, 8 rows in flight per lane;
+//   - the 4 waves take interleaved rows, 16 rows in flight per lane, and the
+//     state moves with non-temporal loads/stores (it is streamed once per step
+//     and is larger than any cache, so it should not displace other lines);
 //   - the state row is updated in registers and reused for y without a
 //     re-read; the partial y of the 4 waves is summed through LDS.
 #include "common.h"
@@ -17,9 +19,11 @@
 namespace ret {
 namespace {
 
+typedef float vf4 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kRowsInFlight = 8;
+constexpr int kRowsInFlight = 16;
 
 template <typename T, int VEC>
 __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(const T* __restrict__ q, const T* __restrict__ k,
@@ -63,8 +67,8 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(const T* __res
         const int r = r0 + kWaves * u;
         if (r < dk) {
           if constexpr (VEC == 4) {
-            const float4 t = *reinterpret_cast<const float4*>(Sh + static_cast<long>(r) * dv);
-            s[u][0] = t.x; s[u][1] = t.y; s[u][2] = t.z; s[u][3] = t.w;
+            const vf4 t = __builtin_nontemporal_load(reinterpret_cast<const vf4*>(Sh + static_cast<long>(r) * dv));
+            s[u][0] = t[0]; s[u][1] = t[1]; s[u][2] = t[2]; s[u][3] = t[3];
           } else {
             s[u][0] = Sh[static_cast<long>(r) * dv];
           }
@@ -82,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(const T* __res
             acc[e] = fmaf(qr, s[u][e], acc[e]);
           }
           if constexpr (VEC == 4) {
-            *reinterpret_cast<float4*>(Sh + static_cast<long>(r) * dv) = make_float4(s[u][0], s[u][1], s[u][2], s[u][3]);
+            __builtin_nontemporal_store(vf4{s[u][0], s[u][1], s[u][2], s[u][3]}, reinterpret_cast<vf4*>(Sh + static_cast<long>(r) * dv));
           } else {
             Sh[static_cast<long>(r) * dv] = s[u][0];
           }

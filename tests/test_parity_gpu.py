@@ -71,6 +71,13 @@ CHUNK_CASES = [
     (2, 3, 385, 128, 192, 64, "bf16", True, [0.999, 0.95, 0.5]),
     (1, 2, 70, 256, 64, 16, "bf16", True, [0.9, 0.97]),
     (1, 1, 33, 32, 64, 32, "bf16", False, [1.0]),
+    # every MFMA tile layout: 128-token tiles with two LDS copies (dk 64/128) and
+    # one copy (dk 256), chunk lengths equal to and below the tile
+    (1, 2, 300, 128, 128, 128, "bf16", True, [0.99, 0.7]),
+    (1, 2, 250, 128, 128, 100, "bf16", True, [0.98, 0.5]),
+    (1, 1, 200, 64, 64, 96, "bf16", True, [0.9]),
+    (1, 2, 250, 256, 128, 100, "bf16", True, [0.995, 0.8]),
+    (2, 2, 130, 64, 192, 40, "bf16", True, [0.97, 0.3]),
 ]
 
 
