@@ -143,7 +143,10 @@ size_t retention_chunkwise_workspace_bytes(int B, int H, int T, int dk, int dv, 
   if (B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1 || C < 1) return static_cast<size_t>(-1);
   if (dk > RET_MAX_DK || dv > RET_MAX_DV || C > RET_MAX_CHUNK) return static_cast<size_t>(-1);
   if (dt != RET_F32 && dt != RET_BF16) return static_cast<size_t>(-1);
-  return 0;
+  if (T == 0 || !ret::chunkwise_mfma_supports(T, dk, dv, C, static_cast<int>(dt))) return 0;
+  const ret::ChunkSegments segs = ret::chunkwise_mfma_segments(B, H, T, dv, C);
+  if (segs.nseg <= 1) return 0;
+  return static_cast<size_t>(segs.nseg) * B * H * dk * dv * sizeof(float);
 }
 
 ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, const float* gamma,
@@ -169,6 +172,10 @@ ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, 
   if (overlap(y, ny, q, bht * dk * es) || overlap(y, ny, k, bht * dk * es) || overlap(y, ny, v, ny) ||
       overlap(y, ny, state_in, ns) || overlap(y, ny, state_out, ns))
     return fail(RET_ERR_INVALID_ARG, "%s: y overlaps an input or a state buffer", fn);
+  if (need > 0 && (overlap(workspace, need, y, ny) || overlap(workspace, need, q, bht * dk * es) ||
+                   overlap(workspace, need, k, bht * dk * es) || overlap(workspace, need, v, ny) ||
+                   overlap(workspace, need, state_in, ns) || overlap(workspace, need, state_out, ns)))
+    return fail(RET_ERR_INVALID_ARG, "%s: workspace overlaps another argument", fn);
   if (state_in != state_out && overlap(state_in, ns, state_out, ns))
     return fail(RET_ERR_INVALID_ARG, "%s: state_in and state_out overlap without being the same buffer", fn);
   if (state_out != nullptr && (overlap(state_out, ns, q, bht * dk * es) || overlap(state_out, ns, k, bht * dk * es) ||
@@ -181,8 +188,10 @@ ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, 
     return e == hipSuccess ? ok() : hip_fail(fn, e);
   }
   const bool mfma = ret::chunkwise_mfma_supports(T, dk, dv, C, static_cast<int>(dt));
+  const ret::ChunkSegments segs = mfma ? ret::chunkwise_mfma_segments(B, H, T, dv, C) : ret::ChunkSegments{T, 1};
+  float* ws = static_cast<float*>(workspace);
   return for_head_groups(fn, H, gamma, [&](const ret::HeadGroup& g) {
-    if (mfma) return ret::launch_chunkwise_mfma(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, g, s);
+    if (mfma) return ret::launch_chunkwise_mfma(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, segs, ws, g, s);
     return ret::launch_chunkwise_generic(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, static_cast<int>(dt),
                                          g, s);
   });

@@ -105,12 +105,28 @@ struct Cfg {
   static_assert(KPT >= 1 && VPT >= 1, "tile too small for the staging split");
 };
 
-template <int CT, int DK>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2))) void
+// Sequence segments (long sequences with few heads).  Segment s covers tokens
+// [s*seg_len, (s+1)*seg_len).  ws holds nseg state slots of [B,H,dk,dv] fp32:
+// the state-only pass writes the end state of segment s (started from zero)
+// into slot s+1, the scan turns slot s into the incoming state of segment s,
+// and the full pass starts segment s from slot s.
+struct SegArgs {
+  int seg_len;     // tokens per segment (a multiple of C)
+  int nseg;        // segments; 1 = whole sequence, ws unused
+  int bnh;         // B * heads of this launch
+  float* ws;       // workspace (nseg slots) or null
+  long ws_stride;  // elements per slot (B * H * dk * dv)
+};
+
+// kOut = true: the full kernel (outputs and state, 4 + 4 waves).
+// kOut = false: the state-only pass over segments 0..nseg-2 (4 state waves).
+template <int CT, int DK, bool kOut>
+__global__ __attribute__((amdgpu_flat_work_group_size(kOut ? 512 : 256, kOut ? 512 : 256),
+                          amdgpu_waves_per_eu(kOut ? 2 : 1, 2))) void
 chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                       const uint16_t* __restrict__ v, const float* state_in, float* state_out,
                       uint16_t* __restrict__ y, HeadDecay gam, int H, int h0, int nh, int Tn, int dv, int C,
-                      int ntiles) {
+                      int ntiles, SegArgs sg) {
   using F = Cfg<CT, DK>;
   constexpr int NSP = CT / 32;  // key (token) steps of 32 per chunk tile
   constexpr int NB = F::NBUF;
@@ -125,18 +141,19 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar) by construction
-  const int wr = w & 3;                                      // index within the role
+  const int wr = kOut ? (w & 3) : w;                         // index within the role
   const int c16 = lane & 15;
   const int g = lane >> 4;
 
-  // Workgroup -> (batch, head, column tile).  Consecutive linear ids (the
-  // column tiles of one head) are placed on one XCD (dispatch is round-robin
-  // over the 8 XCDs by workgroup id).
+  // Workgroup -> (segment, batch, head, column tile).  Consecutive linear ids
+  // (the column tiles of one head and segment) are placed on one XCD
+  // (dispatch is round-robin over the 8 XCDs by workgroup id).
   const int total = gridDim.x;
   int lin = blockIdx.x;
   if ((total & 7) == 0) lin = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
   const int tile = lin % ntiles;
-  const int bh = lin / ntiles;
+  const int bh = (lin / ntiles) % sg.bnh;
+  const int seg = lin / ntiles / sg.bnh;
   const int hl = bh % nh;
   const int b = bh / nh;
   const long head = static_cast<long>(b) * H + h0 + hl;
@@ -149,12 +166,17 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   uint16_t* yh = y + head * Tn * dv + col0;
   const long sbase = head * static_cast<long>(DK) * dv + col0;
   const uint32_t vrow = static_cast<uint32_t>(dv) * 2u;  // bytes per V / Y row
-  const int nchunks = (Tn + C - 1) / C;
+  const int t_begin = seg * sg.seg_len;
+  const int t_end = min(Tn, t_begin + sg.seg_len);
+  const int nchunks = (t_end - t_begin + C - 1) / C;
 
-  if (w >= 4) {
+  if (!kOut || w >= 4) {
     // =========================== state waves ===========================
-    const int st = tid - 256;  // staging thread index 0..255
+    const int st = kOut ? tid - 256 : tid;  // staging thread index 0..255
     const int dbase = wr * (DK / 4);
+    // initial state: state_in (one segment), the scanned slot of this segment,
+    // or zero (state-only pass)
+    const float* init = !kOut ? nullptr : (sg.nseg > 1 ? sg.ws + seg * sg.ws_stride : state_in);
     f32x4 Racc[F::RM][4];
 #pragma unroll
     for (int mb = 0; mb < F::RM; ++mb)
@@ -163,7 +185,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int d = dbase + 16 * mb + 4 * g + i;
-          Racc[mb][nb][i] = state_in != nullptr ? state_in[sbase + static_cast<long>(d) * dv + 16 * nb + c16] : 0.0f;
+          Racc[mb][nb][i] = init != nullptr ? init[sbase + static_cast<long>(d) * dv + 16 * nb + c16] : 0.0f;
         }
     auto write_rt = [&](int buf) {
 #pragma unroll
@@ -293,27 +315,30 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     };
 
     {
-      const int L0 = min(C, Tn);
-      load_kv(0, L0);
-      write_rt(0);
+      const int L0 = min(C, t_end - t_begin);
+      load_kv(t_begin, L0);
+      if constexpr (kOut) write_rt(0);
       store_kv(0);
       if constexpr (kVz) store_vz(L0);
-      if constexpr (NB == 2) load_kv(C, C < Tn ? min(C, Tn - C) : 0);  // chunk 1 into registers
+      if constexpr (NB == 2) {
+        const int s1 = t_begin + C;
+        load_kv(s1, s1 < t_end ? min(C, t_end - s1) : 0);  // chunk 1 into registers
+      }
     }
     __syncthreads();  // chunk 0 staged, R_0 published
 
     for (int ci = 0; ci < nchunks; ++ci) {
-      const int s0 = ci * C;
-      const int L = min(C, Tn - s0);
+      const int s0 = t_begin + ci * C;
+      const int L = min(C, t_end - s0);
       const int s1 = s0 + C;
-      const int Ln = s1 < Tn ? min(C, Tn - s1) : 0;
+      const int Ln = s1 < t_end ? min(C, t_end - s1) : 0;
       if constexpr (NB == 2) {
         const int X = ci & 1;
         update(X, L);
-        write_rt(X ^ 1);                 // R_(i+1) into the other copy
-        if (Ln > 0) store_kv(X ^ 1);     // chunk i+1 (loaded during chunk i-1)
+        if constexpr (kOut) write_rt(X ^ 1);  // R_(i+1) into the other copy
+        if (Ln > 0) store_kv(X ^ 1);          // chunk i+1 (loaded during chunk i-1)
         const int s2 = s1 + C;
-        load_kv(s2, s2 < Tn ? min(C, Tn - s2) : 0);  // chunk i+2 into registers
+        load_kv(s2, s2 < t_end ? min(C, t_end - s2) : 0);  // chunk i+2 into registers
         __syncthreads();
       } else {
         // next chunk's K/V, issued unconditionally (an empty buffer past the end
@@ -321,7 +346,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         load_kv(s1, Ln);
         update(0, L);
         __syncthreads();  // output waves are done with R^T, K and V of this chunk
-        write_rt(0);
+        if constexpr (kOut) write_rt(0);
         if (Ln > 0) {
           store_kv(0);
           store_vz(Ln);
@@ -330,7 +355,10 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       }
     }
 
-    if (state_out != nullptr) {
+    // final state: state_out (last segment) or, in the state-only pass, the
+    // slot of the next segment
+    float* fin = kOut ? (seg == sg.nseg - 1 ? state_out : nullptr) : sg.ws + (seg + 1) * sg.ws_stride;
+    if (fin != nullptr) {
 #pragma unroll
       for (int mb = 0; mb < F::RM; ++mb)
 #pragma unroll
@@ -338,10 +366,10 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int d = dbase + 16 * mb + 4 * g + i;
-            state_out[sbase + static_cast<long>(d) * dv + 16 * nb + c16] = Racc[mb][nb][i];
+            fin[sbase + static_cast<long>(d) * dv + 16 * nb + c16] = Racc[mb][nb][i];
           }
     }
-  } else {
+  } else if constexpr (kOut) {
     // =========================== output waves ===========================
     int qblk[F::NQ];
     if constexpr (F::NQ == 2) {
@@ -373,14 +401,14 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         for (int s = 0; s < F::KS; ++s) Qreg[qi][s] = __builtin_bit_cast(bf16x8, buffer_load16(rq, rowoff + 64u * s));
       }
     };
-    load_q(0, min(C, Tn));
+    load_q(t_begin, min(C, t_end - t_begin));
     __syncthreads();  // chunk 0 staged, R_0 published
 
     for (int ci = 0; ci < nchunks; ++ci) {
-      const int s0 = ci * C;
-      const int L = min(C, Tn - s0);
+      const int s0 = t_begin + ci * C;
+      const int L = min(C, t_end - s0);
       const int s1 = s0 + C;
-      const int Ln = s1 < Tn ? min(C, Tn - s1) : 0;
+      const int Ln = s1 < t_end ? min(C, t_end - s1) : 0;
       const int X = NB == 2 ? (ci & 1) : 0;
       const uint16_t* Kx = Ks[X];
       const uint16_t* Vx = Vs[X];
@@ -507,26 +535,67 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   }
 }
 
+// ws slot s <- incoming state of segment s: slot 0 = state_in (or 0), slot s =
+// gamma^seg_len * slot (s-1) + (end state of segment s-1 from zero).
+__global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ ws, const float* state_in,
+                                                           HeadDecay gam, int H, int h0, int nh, int B, long per_head,
+                                                           int nseg, int seg_len, long stride) {
+  const long n = static_cast<long>(B) * nh * per_head;
+  for (long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x; idx < n;
+       idx += static_cast<long>(gridDim.x) * blockDim.x) {
+    const long bh = idx / per_head;
+    const long within = idx % per_head;
+    const int hl = static_cast<int>(bh % nh);
+    const long head = (bh / nh) * H + h0 + hl;
+    const long off = head * per_head + within;
+    const float gs = gamma_pow(gam.log2g[hl], seg_len);
+    float s = state_in != nullptr ? state_in[off] : 0.0f;
+    ws[off] = s;
+    for (int sg = 1; sg < nseg; ++sg) {
+      s = fmaf(gs, s, ws[sg * stride + off]);
+      ws[sg * stride + off] = s;
+    }
+  }
+}
+
 template <int CT, int DK>
 hipError_t launch_cfg(const void* q, const void* k, const void* v, const float* state_in, float* state_out, void* y,
-                      int B, int H, int Tn, int dv, int C, const HeadDecay& hd, const HeadGroup& g, hipStream_t s) {
+                      int B, int H, int Tn, int dv, int C, const HeadDecay& hd, const HeadGroup& g,
+                      const ChunkSegments& segs, float* ws, hipStream_t s) {
   const int ntiles = dv / kTN;
-  const int total = B * g.nh * ntiles;
-  hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK>), dim3(total), dim3(Cfg<CT, DK>::kThreads), 0, s,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), state_in, state_out, static_cast<uint16_t*>(y), hd, H, g.h0,
-                     g.nh, Tn, dv, C, ntiles);
+  const int bnh = B * g.nh;
+  SegArgs sg{segs.seg_len, segs.nseg, bnh, ws, static_cast<long>(B) * H * DK * dv};
+  const uint16_t* qp = static_cast<const uint16_t*>(q);
+  const uint16_t* kp = static_cast<const uint16_t*>(k);
+  const uint16_t* vp = static_cast<const uint16_t*>(v);
+  uint16_t* yp = static_cast<uint16_t*>(y);
+  if (segs.nseg > 1) {
+    // end states of segments 0..nseg-2 from zero, then the scan over segments
+    hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, false>), dim3(bnh * ntiles * (segs.nseg - 1)), dim3(256), 0, s,
+                       qp, kp, vp, nullptr, nullptr, yp, hd, H, g.h0, g.nh, Tn, dv, C, ntiles, sg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long per_head = static_cast<long>(DK) * dv;
+    const long n = static_cast<long>(bnh) * per_head;
+    const unsigned blocks = static_cast<unsigned>(min(65536L, (n + 255) / 256));
+    hipLaunchKernelGGL(segment_scan_kernel, dim3(blocks), dim3(256), 0, s, ws, state_in, hd, H, g.h0, g.nh, B,
+                       per_head, segs.nseg, segs.seg_len, sg.ws_stride);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, true>), dim3(bnh * ntiles * segs.nseg), dim3(512), 0, s, qp, kp, vp,
+                     state_in, state_out, yp, hd, H, g.h0, g.nh, Tn, dv, C, ntiles, sg);
   return hipGetLastError();
 }
 
 template <int CT>
 hipError_t launch_ct(const void* q, const void* k, const void* v, const float* state_in, float* state_out, void* y,
                      int B, int H, int Tn, int dk, int dv, int C, const HeadDecay& hd, const HeadGroup& g,
-                     hipStream_t s) {
+                     const ChunkSegments& segs, float* ws, hipStream_t s) {
   switch (dk) {
-    case 64: return launch_cfg<CT, 64>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, s);
-    case 128: return launch_cfg<CT, 128>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, s);
-    default: return launch_cfg<CT, 256>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, s);
+    case 64: return launch_cfg<CT, 64>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
+    case 128: return launch_cfg<CT, 128>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
+    default: return launch_cfg<CT, 256>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
   }
 }
 
@@ -536,12 +605,31 @@ bool chunkwise_mfma_supports(int /*T*/, int dk, int dv, int C, int dt) {
   return dt == 1 && (dk == 64 || dk == 128 || dk == 256) && dv % kTN == 0 && C >= 1 && C <= 128;
 }
 
+// A call whose (batch, head, column tile) walkers fill fewer than
+// kTargetWorkgroups compute units is split into sequence segments (each at
+// least kMinSegChunks chunks long) so that the walkers cover the device.
+ChunkSegments chunkwise_mfma_segments(int B, int H, int T, int dv, int C) {
+  constexpr long kTargetWorkgroups = 256;  // MI355X compute units
+  constexpr int kMinSegChunks = 8;
+  ChunkSegments r{T > 0 ? T : 1, 1};
+  const long walkers = static_cast<long>(B) * H * (dv / kTN);
+  const long nchunks = (static_cast<long>(T) + C - 1) / C;
+  if (walkers < 1 || walkers >= kTargetWorkgroups || nchunks < 2 * kMinSegChunks) return r;
+  long want = (kTargetWorkgroups + walkers - 1) / walkers;
+  want = min(want, nchunks / kMinSegChunks);
+  if (want < 2) return r;
+  const long per = (nchunks + want - 1) / want;  // chunks per segment
+  r.seg_len = static_cast<int>(per * C);
+  r.nseg = static_cast<int>((nchunks + per - 1) / per);
+  return r;
+}
+
 hipError_t launch_chunkwise_mfma(const void* q, const void* k, const void* v, const float* state_in,
                                  float* state_out, void* y, int B, int H, int T, int dk, int dv, int C,
-                                 const HeadGroup& g, hipStream_t s) {
+                                 const ChunkSegments& segs, float* ws, const HeadGroup& g, hipStream_t s) {
   const HeadDecay hd = make_head_decay(g);
-  if (C <= 64) return launch_ct<64>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, hd, g, s);
-  return launch_ct<128>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, hd, g, s);
+  if (C <= 64) return launch_ct<64>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, hd, g, segs, ws, s);
+  return launch_ct<128>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, hd, g, segs, ws, s);
 }
 
 }  // namespace ret

@@ -37,9 +37,17 @@ hipError_t launch_chunkwise_generic(const void* q, const void* k, const void* v,
 
 // bf16 MFMA chunkwise kernel; chunkwise_mfma_supports() says whether it takes a shape.
 bool chunkwise_mfma_supports(int T, int dk, int dv, int C, int dt);
+// Sequence segmentation of an MFMA call: nseg segments of seg_len tokens
+// (nseg = 1: no segmentation, no workspace).  A pure function of the sizes.
+struct ChunkSegments {
+  int seg_len;
+  int nseg;
+};
+ChunkSegments chunkwise_mfma_segments(int B, int H, int T, int dv, int C);
+// ws: nseg * B*H*dk*dv fp32 when segs.nseg > 1 (else unused)
 hipError_t launch_chunkwise_mfma(const void* q, const void* k, const void* v, const float* state_in,
                                  float* state_out, void* y, int B, int H, int T, int dk, int dv, int C,
-                                 const HeadGroup& g, hipStream_t s);
+                                 const ChunkSegments& segs, float* ws, const HeadGroup& g, hipStream_t s);
 
 // Copies state_in (or zeros when null) into state_out: the T = 0 case.
 hipError_t launch_state_copy(const float* state_in, float* state_out, size_t n, hipStream_t s);

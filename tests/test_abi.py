@@ -107,6 +107,31 @@ def test_workspace_query(lib):
     assert lib.retention_chunkwise_workspace_bytes(1, 2, 64, 16, 16, 16, 5) == bad
 
 
+def test_workspace_for_segmented_long_sequences(lib):
+    """bf16 calls with few (batch, head, 64-column) walkers over a long sequence
+    are split into sequence segments: one fp32 state slot per segment."""
+    # B1 H8 T65536 dk256 dv512 C128: 64 walkers -> 4 segments of 16384 tokens
+    assert lib.retention_chunkwise_workspace_bytes(1, 8, 65536, 256, 512, 128, 1) == 4 * 8 * 256 * 512 * 4
+    # 256 walkers (B4 H8 dv512) fill the device: no segments
+    assert lib.retention_chunkwise_workspace_bytes(4, 8, 2048, 256, 512, 64, 1) == 0
+    # short sequences (fewer than 16 chunks) and fp32 calls never segment
+    assert lib.retention_chunkwise_workspace_bytes(1, 1, 15 * 64, 64, 64, 64, 1) == 0
+    assert lib.retention_chunkwise_workspace_bytes(1, 1, 65536, 64, 64, 64, 0) == 0
+    # 1 walker, 32 chunks: at most T/(8 chunks) = 4 segments
+    assert lib.retention_chunkwise_workspace_bytes(1, 1, 2048, 64, 64, 64, 1) == 4 * 64 * 64 * 4
+
+
+def test_segmented_call_requires_workspace(lib):
+    q, k, v, y = (ctypes.c_void_p(a << 36) for a in (1, 2, 3, 4))
+    args = dict(q=q, k=k, v=v, y=y, B=1, H=1, T=2048, dk=64, dv=64, C=64, dt=1)
+    need = lib.retention_chunkwise_workspace_bytes(1, 1, 2048, 64, 64, 64, 1)
+    assert chunk(lib, **args) == INVALID and "workspace" in _lib.last_error()
+    assert chunk(lib, ws=ctypes.c_void_p(5 << 36), wsb=need - 16, **args) == INVALID
+    assert "workspace" in _lib.last_error()
+    assert chunk(lib, ws=ctypes.c_void_p((4 << 36) + 4096), wsb=need, **args) == INVALID
+    assert "workspace overlaps" in _lib.last_error()
+
+
 def test_error_text_is_cleared_by_success_path_query(lib):
     chunk(lib, B=0)
     assert _lib.last_error() != ""
@@ -120,3 +145,20 @@ def test_python_wrapper_refuses_cpu_tensors():
         _lib.chunkwise_fwd(q, q, q, [0.5], 4)
     with pytest.raises(ValueError):
         _lib.recurrent_step(q[0], q[0], q[0], [0.5], torch.zeros(1, 1, 4, 4))
+
+
+def test_host_dispatch_of_every_parity_shape_without_a_device(lib):
+    """With no GPU present, every chunkwise parity shape passes validation and
+    segment planning on the host and fails only at the launch (RET_ERR_HIP).
+    Skipped where a GPU is visible: the pointers here are placeholders."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("placeholder pointers must never reach a real device")
+    import test_parity_gpu as parity
+    for (B, H, T, dk, dv, C, dt, _, _) in parity.CHUNK_CASES:
+        d = 1 if dt == "bf16" else 0
+        need = lib.retention_chunkwise_workspace_bytes(B, H, T, dk, dv, C, d)
+        q, k, v, y, w = (ctypes.c_void_p(a << 36) for a in (1, 2, 3, 4, 5))
+        st = lib.retention_chunkwise_fwd(q, k, v, gam(*([0.5] * H)), None, None, y, B, H, T, dk, dv, C, d,
+                                         w if need else None, need, None)
+        assert st == 3, (B, H, T, dk, dv, C, dt, _lib.last_error())

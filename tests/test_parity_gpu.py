@@ -78,6 +78,13 @@ CHUNK_CASES = [
     (1, 1, 200, 64, 64, 96, "bf16", True, [0.9]),
     (1, 2, 250, 256, 128, 100, "bf16", True, [0.995, 0.8]),
     (2, 2, 130, 64, 192, 40, "bf16", True, [0.97, 0.3]),
+    # few (batch, head, column tile) walkers over a long sequence: split into
+    # sequence segments (state-only pass, scan over segments, full pass)
+    (1, 1, 2048, 64, 64, 64, "bf16", True, [0.99]),
+    (1, 2, 3000, 128, 192, 40, "bf16", True, [0.995, 0.9]),
+    (1, 1, 4097, 256, 64, 128, "bf16", True, [0.999]),
+    (1, 1, 1024, 64, 64, 1, "bf16", False, [0.97]),
+    (1, 2, 2500, 256, 128, 100, "bf16", False, [1.0, 0.0]),
 ]
 
 
@@ -144,6 +151,31 @@ def test_split_sequence_with_state_handoff(dt):
     check("split y", torch.cat([y1, y2], dim=2), y_ref, tol(q.dtype))
     check("split state", st, s_ref, tol(q.dtype))
     check("split vs one call", torch.cat([y1, y2], dim=2), y_all, tol(q.dtype))
+
+
+def test_segmented_handoff_in_place_and_explicit_workspace():
+    """Segmented calls (few heads, long sequence) with state_out aliasing
+    state_in, and a caller-provided workspace that starts out as NaN."""
+    B, H, T, dk, dv, C = 1, 2, 3000, 128, 128, 64
+    say("segmented handoff, in-place state, NaN-filled workspace")
+    gs = [0.999, 0.9]
+    q, k, v, s0 = make_inputs(B, H, T, dk, dv, "bf16", seed=7, with_state=True)
+    qd, kd, vd, sd = to_dev(q, k, v, s0)
+    t = 1100
+    parts = [(0, t), (t, T)]
+    for a, b in parts:
+        assert ret.chunkwise_workspace_bytes(B, H, b - a, dk, dv, C, qd.dtype) > 0
+    st = sd.clone()
+    ys = []
+    for a, b in parts:
+        need = ret.chunkwise_workspace_bytes(B, H, b - a, dk, dv, C, qd.dtype)
+        ws = torch.full((need // 4 + 64,), float("nan"), device=DEV)
+        y, _ = ret.chunkwise_fwd(qd[:, :, a:b].contiguous(), kd[:, :, a:b].contiguous(), vd[:, :, a:b].contiguous(),
+                                 gs, C, state_in=st, state_out=st, workspace=ws.view(torch.uint8))
+        ys.append(y)
+    y_ref, s_ref = oracle.recurrent(q, k, v, torch.tensor(gs, dtype=torch.float32), s0)
+    check("segmented split y", torch.cat(ys, dim=2), y_ref, 2e-2)
+    check("segmented split state", st, s_ref, 2e-2)
 
 
 def test_empty_sequence_copies_state():
