@@ -69,6 +69,16 @@ __device__ __forceinline__ bf16x8 join(s16x4 lo, s16x4 hi) {
 
 __device__ __forceinline__ bf16x8 lds_read16(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
+// Workgroup barrier for hand-offs through LDS.  The fences cover LDS only, so
+// a wave waits for its own LDS accesses but not for its global loads and
+// stores in flight: the K/V/Q loads of later chunks and the Y stores stay
+// outstanding across the barrier (a __syncthreads() fence would drain them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -81,8 +91,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 buffer_load16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
 }
-__device__ __forceinline__ void buffer_store2(rsrc_t r, uint32_t off, uint16_t x) {
-  __builtin_amdgcn_raw_buffer_store_b16(x, r, static_cast<int>(off), 0, 0);
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void buffer_store8(rsrc_t r, uint32_t off, u32x2 x) {
+  __builtin_amdgcn_raw_buffer_store_b64(x, r, static_cast<int>(off), 0, 0);
 }
 
 template <int CT, int DK>
@@ -120,7 +131,14 @@ struct SegArgs {
 
 // kOut = true: the full kernel (outputs and state, 4 + 4 waves).
 // kOut = false: the state-only pass over segments 0..nseg-2 (4 state waves).
-template <int CT, int DK, bool kOut>
+// kZS = true: V is staged in LDS already scaled by zeta_t = gamma^(L-1-t), once
+// per element, and serves both the state update and the outputs.  The
+// outputs then use P' = (Q K^T .* causal mask) diag-scaled by gamma^(j-L+1)
+// per query row j, since gamma^(j-t) V_t = gamma^(j-L+1) zeta_t V_t.  The
+// factors stay within 2^+-100 when gamma^(CT-1) >= 2^-100 (the host checks
+// this for every head of the launch).  kZS = false keeps V unscaled and
+// applies zeta to the update's operand in registers (any gamma in [0, 1]).
+template <int CT, int DK, bool kOut, bool kZS>
 __global__ __attribute__((amdgpu_flat_work_group_size(kOut ? 512 : 256, kOut ? 512 : 256),
                           amdgpu_waves_per_eu(kOut ? 2 : 1, 2))) void
 chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -135,7 +153,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   __shared__ __attribute__((aligned(16))) uint16_t Rt[NB][kTN * F::RLD];
   // With one LDS copy there is room for zeta*V, formed once when V is staged;
   // with two copies zeta is applied to the update's V operand in registers.
-  constexpr bool kVz = NB == 1;
+  constexpr bool kVz = NB == 1 && !kZS;
   __shared__ __attribute__((aligned(16))) uint16_t Vz[kVz ? CT * F::VLD : 8];
 
   const int tid = threadIdx.x;
@@ -196,42 +214,55 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
           *reinterpret_cast<bf16x4*>(&Rt[buf][(16 * nb + c16) * F::RLD + dbase + 16 * mb + 4 * g]) = r;
         }
     };
-    // Staging map: groups of 8 lanes read 128 contiguous bytes per instruction;
-    // a thread's pieces are 128 bytes (K) or one row (V) apart, so the
-    // per-piece offsets fit the instructions' immediate offset field.
+    // Staging map (16-byte pieces; round r adds r * rows-per-round rows).
+    // Rows of 16 or more pieces (d_k >= 128): each 16-lane group moves 256
+    // contiguous bytes of one row.  Rows of 8 pieces (d_k = 64, and V): a
+    // 16-lane group moves rows x and x+8, which the 144-byte LDS stride places
+    // 32 banks apart.  Either way a group's LDS writes hit 64 distinct banks.
+    constexpr int KPR = DK / 8;       // pieces per K row
+    constexpr int KRR = 256 / KPR;    // K rows per round
+    const int prow = (st >> 4 & 7) + 16 * (st >> 7) + 8 * (st >> 3 & 1);  // paired-row map, 32 rows per round
+    const int krow = KPR == 8 ? prow : st / KPR;
+    const int kc8 = KPR == 8 ? (st & 7) : st % KPR;
+    const int vc8 = st & 7;
     u32x4 kreg[F::KPT];
     u32x4 vreg[F::VPT];
-    const int grp = st >> 3, gl = st & 7;
-    const uint32_t koff = static_cast<uint32_t>(grp * 8 * F::KPT + gl) * 16u;  // + 128 r
-    const int vrow0 = grp * F::VPT;                                            // rows vrow0 + r
-    const uint32_t voff = static_cast<uint32_t>(vrow0) * vrow + 16u * gl;      // + r * vrow
+    const uint32_t koff = static_cast<uint32_t>(krow * DK + 8 * kc8) * 2u;  // + r * KRR rows
+    const uint32_t voff = static_cast<uint32_t>(prow) * vrow + 16u * vc8;   // + r * 32 rows
     auto load_kv = [&](int s1, int Ln) {
       const rsrc_t rk = make_rsrc(kh + static_cast<long>(s1) * DK, static_cast<uint32_t>(Ln) * DK * 2u);
 #pragma unroll
-      for (int r = 0; r < F::KPT; ++r) kreg[r] = buffer_load16(rk, koff + 128u * r);
+      for (int r = 0; r < F::KPT; ++r) kreg[r] = buffer_load16(rk, koff + static_cast<uint32_t>(r * KRR * DK * 2));
       const rsrc_t rv = make_rsrc(vh + static_cast<long>(s1) * dv,
                                   Ln > 0 ? static_cast<uint32_t>(Ln - 1) * vrow + kTN * 2u : 0u);
 #pragma unroll
-      for (int r = 0; r < F::VPT; ++r) vreg[r] = buffer_load16(rv, voff + vrow * r);
+      for (int r = 0; r < F::VPT; ++r) vreg[r] = buffer_load16(rv, voff + 32u * vrow * r);
     };
-    auto store_kv = [&](int buf) {
+    // Ln: length of the chunk being staged (zeta of its rows when kZS)
+    auto store_kv = [&](int buf, int Ln) {
 #pragma unroll
-      for (int r = 0; r < F::KPT; ++r) {
-        const int p = grp * 8 * F::KPT + 8 * r + gl;
-        const int row = p / (DK / 8), c8 = p % (DK / 8);
-        *reinterpret_cast<u32x4*>(&Ks[buf][row * F::KLD + 8 * c8]) = kreg[r];
+      for (int r = 0; r < F::KPT; ++r)
+        *reinterpret_cast<u32x4*>(&Ks[buf][(krow + r * KRR) * F::KLD + 8 * kc8]) = kreg[r];
+#pragma unroll
+      for (int r = 0; r < F::VPT; ++r) {
+        const int row = prow + 32 * r;
+        if constexpr (kZS) {
+          const float z = row < Ln ? gamma_pow(lg, Ln - 1 - row) : 0.0f;
+          const f32x8 vf = __builtin_convertvector(__builtin_bit_cast(bf16x8, vreg[r]), f32x8) * z;
+          *reinterpret_cast<bf16x8*>(&Vs[buf][row * F::VLD + 8 * vc8]) = __builtin_convertvector(vf, bf16x8);
+        } else {
+          *reinterpret_cast<u32x4*>(&Vs[buf][row * F::VLD + 8 * vc8]) = vreg[r];
+        }
       }
-#pragma unroll
-      for (int r = 0; r < F::VPT; ++r) *reinterpret_cast<u32x4*>(&Vs[buf][(vrow0 + r) * F::VLD + 8 * gl]) = vreg[r];
     };
     // zeta*V for the one-copy layout: zeta_row = gamma^(L-1-row), 0 past the chunk end
     auto store_vz = [&](int Ln) {
 #pragma unroll
       for (int r = 0; r < F::VPT; ++r) {
-        const int row = vrow0 + r;
+        const int row = prow + 32 * r;
         const float z = row < Ln ? gamma_pow(lg, Ln - 1 - row) : 0.0f;
         const f32x8 vf = __builtin_convertvector(__builtin_bit_cast(bf16x8, vreg[r]), f32x8) * z;
-        *reinterpret_cast<bf16x8*>(&Vz[row * F::VLD + 8 * gl]) = __builtin_convertvector(vf, bf16x8);
+        *reinterpret_cast<bf16x8*>(&Vz[row * F::VLD + 8 * vc8]) = __builtin_convertvector(vf, bf16x8);
       }
     };
     // zeta_t = gamma^(L-1-t) for the tokens t = 32s + 8g + 2(e%4) + e/4 this lane
@@ -287,7 +318,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
           read_step(s, 0);
         }
         // zeta-scale the V operand of step s (in place)
-        if constexpr (!kVz) {
+        if constexpr (!kVz && !kZS) {
         float z[8];
         if (L == CT) {  // a full tile: every token group lies inside the chunk
 #pragma unroll
@@ -318,14 +349,14 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       const int L0 = min(C, t_end - t_begin);
       load_kv(t_begin, L0);
       if constexpr (kOut) write_rt(0);
-      store_kv(0);
+      store_kv(0, L0);
       if constexpr (kVz) store_vz(L0);
       if constexpr (NB == 2) {
         const int s1 = t_begin + C;
         load_kv(s1, s1 < t_end ? min(C, t_end - s1) : 0);  // chunk 1 into registers
       }
     }
-    __syncthreads();  // chunk 0 staged, R_0 published
+    lds_barrier();  // chunk 0 staged, R_0 published
 
     for (int ci = 0; ci < nchunks; ++ci) {
       const int s0 = t_begin + ci * C;
@@ -336,22 +367,22 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         const int X = ci & 1;
         update(X, L);
         if constexpr (kOut) write_rt(X ^ 1);  // R_(i+1) into the other copy
-        if (Ln > 0) store_kv(X ^ 1);          // chunk i+1 (loaded during chunk i-1)
+        if (Ln > 0) store_kv(X ^ 1, Ln);      // chunk i+1 (loaded during chunk i-1)
         const int s2 = s1 + C;
         load_kv(s2, s2 < t_end ? min(C, t_end - s2) : 0);  // chunk i+2 into registers
-        __syncthreads();
+        lds_barrier();
       } else {
         // next chunk's K/V, issued unconditionally (an empty buffer past the end
         // reads zeros) so the wait counts stay exact; written after the barrier
         load_kv(s1, Ln);
         update(0, L);
-        __syncthreads();  // output waves are done with R^T, K and V of this chunk
+        lds_barrier();  // output waves are done with R^T, K and V of this chunk
         if constexpr (kOut) write_rt(0);
         if (Ln > 0) {
-          store_kv(0);
-          store_vz(Ln);
+          store_kv(0, Ln);
+          if constexpr (kVz) store_vz(Ln);
         }
-        __syncthreads();  // R_(i+1) and the next chunk's K/V are in LDS
+        lds_barrier();  // R_(i+1) and the next chunk's K/V are in LDS
       }
     }
 
@@ -402,7 +433,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       }
     };
     load_q(t_begin, min(C, t_end - t_begin));
-    __syncthreads();  // chunk 0 staged, R_0 published
+    lds_barrier();  // chunk 0 staged, R_0 published
 
     for (int ci = 0; ci < nchunks; ++ci) {
       const int s0 = t_begin + ci * C;
@@ -414,7 +445,9 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       const uint16_t* Vx = Vs[X];
       const uint16_t* Rx = Rt[X];
 
-      // cross-chunk term first: O = gamma^(j+1) (Q R_i), then P V accumulates on top
+      // cross-chunk term first: O^T = (R_i^T Q^T) diag(gamma^(j+1)), then V^T P^T
+      // accumulates on top.  O^T[16nb + 4g + i][query c16] sits in lane
+      // (g, c16): four consecutive value columns of one query row.
       f32x4 O[F::NQ][4];
       {
         bf16x8 rb[2][4];
@@ -431,17 +464,18 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
           for (int qi = 0; qi < F::NQ; ++qi)
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
-              O[qi][nb] = mfma(Qreg[qi][s], rb[s & 1][nb], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : O[qi][nb]);
+              O[qi][nb] = mfma(rb[s & 1][nb], Qreg[qi][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : O[qi][nb]);
         }
       }
+      float rowf[F::NQ];  // gamma^(j-L+1) for this lane's query row j (kZS)
 #pragma unroll
-      for (int qi = 0; qi < F::NQ; ++qi)
+      for (int qi = 0; qi < F::NQ; ++qi) {
+        const int j = 16 * qblk[qi] + c16;
+        const float xi = gamma_pow(lg, j + 1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float xi = gamma_pow(lg, 16 * qblk[qi] + 4 * g + i + 1);
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb) O[qi][nb][i] *= xi;
-        }
+        for (int nb = 0; nb < 4; ++nb) O[qi][nb] *= xi;
+        rowf[qi] = kZS ? exp2f(static_cast<float>(j - L + 1) * lg) : 1.0f;
+      }
 
       // intra-chunk term: key steps of 32 keys on or below the diagonal.  When
       // the scores of all key steps fit in registers (64-token tiles), every
@@ -469,7 +503,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       };
       auto pv = [&](int sp) {
         const int slot = kAllScoresFirst ? sp : 0;
-        // V operands (keys 32sp+4g+e and 32sp+16+4g+e), shared by the wave's query blocks
+        // V^T operands (keys 32sp+4g+e and 32sp+16+4g+e), shared by the wave's query blocks
         bf16x8 vb[4];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
@@ -485,19 +519,26 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int m = qblk[qi] - (2 * sp + h);  // wave-uniform
-            const float boff = m > 0 ? exp2f(static_cast<float>(16 * m + lane_off) * lg) : 0.0f;
+            if constexpr (kZS) {
+              // P' = S .* causal mask, times gamma^(j-L+1) of this lane's row
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float f;
-              if (m > 0) f = boff * cst[e];
-              else if (m == 0) f = Ddg[e];
-              else f = 0.0f;
-              p[4 * h + e] = m >= 0 ? St[qi][slot][h][e] * f : 0.0f;
+              for (int e = 0; e < 4; ++e)
+                p[4 * h + e] = (m > 0 || (m == 0 && 4 * g + e <= c16)) ? St[qi][slot][h][e] * rowf[qi] : 0.0f;
+            } else {
+              const float boff = m > 0 ? exp2f(static_cast<float>(16 * m + lane_off) * lg) : 0.0f;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                float f;
+                if (m > 0) f = boff * cst[e];
+                else if (m == 0) f = Ddg[e];
+                else f = 0.0f;
+                p[4 * h + e] = m >= 0 ? St[qi][slot][h][e] * f : 0.0f;
+              }
             }
           }
           const bf16x8 pa = __builtin_convertvector(p, bf16x8);
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) O[qi][nb] = mfma(pa, vb[nb], O[qi][nb]);
+          for (int nb = 0; nb < 4; ++nb) O[qi][nb] = mfma(vb[nb], pa, O[qi][nb]);
         }
       };
       if constexpr (kAllScoresFirst) {
@@ -517,20 +558,22 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         }
         load_q(s1, Ln);
       }
-      if constexpr (NB == 1) __syncthreads();  // this chunk's K, V and R^T are no longer read
-      // store Y rows (rows past the chunk end fall outside the buffer and are dropped)
+      if constexpr (NB == 1) lds_barrier();  // this chunk's K, V and R^T are no longer read
+      // store Y rows, 4 columns (8 bytes) per lane and block (rows past the
+      // chunk end fall outside the buffer and are dropped)
       {
         const rsrc_t ry = make_rsrc(yh + static_cast<long>(s0) * dv, static_cast<uint32_t>(L - 1) * vrow + kTN * 2u);
 #pragma unroll
-        for (int qi = 0; qi < F::NQ; ++qi)
+        for (int qi = 0; qi < F::NQ; ++qi) {
+          const uint32_t roff = static_cast<uint32_t>(16 * qblk[qi] + c16) * vrow + 8u * g;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t roff = static_cast<uint32_t>(16 * qblk[qi] + 4 * g + i) * vrow + 2u * c16;
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) buffer_store2(ry, roff + 32u * nb, f32_to_bf16(O[qi][nb][i]));
+          for (int nb = 0; nb < 4; ++nb) {
+            const bf16x4 o = __builtin_convertvector(O[qi][nb], bf16x4);
+            buffer_store8(ry, roff + 32u * nb, __builtin_bit_cast(u32x2, o));
           }
+        }
       }
-      __syncthreads();  // the next chunk's R^T, K and V are in LDS
+      lds_barrier();  // the next chunk's R^T, K and V are in LDS
     }
   }
 }
@@ -558,7 +601,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ w
   }
 }
 
-template <int CT, int DK>
+template <int CT, int DK, bool kZS>
 hipError_t launch_cfg(const void* q, const void* k, const void* v, const float* state_in, float* state_out, void* y,
                       int B, int H, int Tn, int dv, int C, const HeadDecay& hd, const HeadGroup& g,
                       const ChunkSegments& segs, float* ws, hipStream_t s) {
@@ -571,7 +614,7 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, const float* 
   uint16_t* yp = static_cast<uint16_t*>(y);
   if (segs.nseg > 1) {
     // end states of segments 0..nseg-2 from zero, then the scan over segments
-    hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, false>), dim3(bnh * ntiles * (segs.nseg - 1)), dim3(256), 0, s,
+    hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, false, kZS>), dim3(bnh * ntiles * (segs.nseg - 1)), dim3(256), 0, s,
                        qp, kp, vp, nullptr, nullptr, yp, hd, H, g.h0, g.nh, Tn, dv, C, ntiles, sg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -583,19 +626,19 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, const float* 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, true>), dim3(bnh * ntiles * segs.nseg), dim3(512), 0, s, qp, kp, vp,
+  hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, true, kZS>), dim3(bnh * ntiles * segs.nseg), dim3(512), 0, s, qp, kp, vp,
                      state_in, state_out, yp, hd, H, g.h0, g.nh, Tn, dv, C, ntiles, sg);
   return hipGetLastError();
 }
 
-template <int CT>
+template <int CT, bool kZS>
 hipError_t launch_ct(const void* q, const void* k, const void* v, const float* state_in, float* state_out, void* y,
                      int B, int H, int Tn, int dk, int dv, int C, const HeadDecay& hd, const HeadGroup& g,
                      const ChunkSegments& segs, float* ws, hipStream_t s) {
   switch (dk) {
-    case 64: return launch_cfg<CT, 64>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
-    case 128: return launch_cfg<CT, 128>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
-    default: return launch_cfg<CT, 256>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
+    case 64: return launch_cfg<CT, 64, kZS>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
+    case 128: return launch_cfg<CT, 128, kZS>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
+    default: return launch_cfg<CT, 256, kZS>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
   }
 }
 
@@ -628,8 +671,16 @@ hipError_t launch_chunkwise_mfma(const void* q, const void* k, const void* v, co
                                  float* state_out, void* y, int B, int H, int T, int dk, int dv, int C,
                                  const ChunkSegments& segs, float* ws, const HeadGroup& g, hipStream_t s) {
   const HeadDecay hd = make_head_decay(g);
-  if (C <= 64) return launch_ct<64>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, hd, g, segs, ws, s);
-  return launch_ct<128>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, hd, g, segs, ws, s);
+  // zeta-staged V when gamma^(CT-1) >= 2^-100 for every head of the group
+  const int ct = C <= 64 ? 64 : 128;
+  bool zs = true;
+  for (int i = 0; i < g.nh; ++i) zs = zs && static_cast<double>(ct - 1) * hd.log2g[i] >= -100.0;
+  if (C <= 64) {
+    if (zs) return launch_ct<64, true>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, hd, g, segs, ws, s);
+    return launch_ct<64, false>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, hd, g, segs, ws, s);
+  }
+  if (zs) return launch_ct<128, true>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, hd, g, segs, ws, s);
+  return launch_ct<128, false>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, hd, g, segs, ws, s);
 }
 
 }  // namespace ret

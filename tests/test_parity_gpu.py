@@ -78,6 +78,9 @@ CHUNK_CASES = [
     (1, 1, 200, 64, 64, 96, "bf16", True, [0.9]),
     (1, 2, 250, 256, 128, 100, "bf16", True, [0.995, 0.8]),
     (2, 2, 130, 64, 192, 40, "bf16", True, [0.97, 0.3]),
+    # zeta-staged V near its limit gamma^(tile-1) = 2^-99 (64- and 128-token tiles)
+    (1, 2, 200, 64, 64, 64, "bf16", True, [0.3367, 0.5]),
+    (1, 2, 300, 128, 64, 128, "bf16", True, [0.5823, 0.9]),
     # few (batch, head, column tile) walkers over a long sequence: split into
     # sequence segments (state-only pass, scan over segments, full pass)
     (1, 1, 2048, 64, 64, 64, "bf16", True, [0.99]),
