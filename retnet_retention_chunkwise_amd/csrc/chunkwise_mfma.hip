@@ -422,20 +422,26 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       Ddg[e] = d >= 0 ? gamma_pow(lg, d) : 0.0f;
     }
     const int lane_off = c16 - 4 * g - 3;
-    bf16x8 Qreg[F::NQ][F::KS];
-    auto load_q = [&](int s1, int Ln) {
+    // Q operand registers.  With one query block per wave there is room for
+    // two copies: the next chunk's Q is loaded at the start of a chunk, a
+    // whole chunk ahead of its use; otherwise it is loaded after the scores.
+    constexpr bool kQ2 = F::NQ == 1;
+    typedef bf16x8 QTile[F::NQ][F::KS];
+    QTile Qa, Qb;
+    auto load_q = [&](QTile& Qd, int s1, int Ln) {
       const rsrc_t rq = make_rsrc(qh + static_cast<long>(s1) * DK, static_cast<uint32_t>(Ln) * DK * 2u);
 #pragma unroll
       for (int qi = 0; qi < F::NQ; ++qi) {
         const uint32_t rowoff = static_cast<uint32_t>(16 * qblk[qi] + c16) * DK * 2u + 16u * g;
 #pragma unroll
-        for (int s = 0; s < F::KS; ++s) Qreg[qi][s] = __builtin_bit_cast(bf16x8, buffer_load16(rq, rowoff + 64u * s));
+        for (int s = 0; s < F::KS; ++s) Qd[qi][s] = __builtin_bit_cast(bf16x8, buffer_load16(rq, rowoff + 64u * s));
       }
     };
-    load_q(t_begin, min(C, t_end - t_begin));
+    load_q(Qa, t_begin, min(C, t_end - t_begin));
     lds_barrier();  // chunk 0 staged, R_0 published
 
-    for (int ci = 0; ci < nchunks; ++ci) {
+    // one chunk with Q in Qreg; Qnext receives the next chunk's Q (kQ2)
+    auto chunk = [&](int ci, QTile& Qreg, QTile& Qnext) {
       const int s0 = t_begin + ci * C;
       const int L = min(C, t_end - s0);
       const int s1 = s0 + C;
@@ -444,6 +450,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       const uint16_t* Kx = Ks[X];
       const uint16_t* Vx = Vs[X];
       const uint16_t* Rx = Rt[X];
+      if constexpr (kQ2) load_q(Qnext, s1, Ln);
 
       // cross-chunk term first: O^T = (R_i^T Q^T) diag(gamma^(j+1)), then V^T P^T
       // accumulates on top.  O^T[16nb + 4g + i][query c16] sits in lane
@@ -545,7 +552,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
         for (int sp = 0; sp < NSP; ++sp)
           if (2 * sp <= qmax) scores(sp);
-        load_q(s1, Ln);  // the Q operand registers are free now
+        if constexpr (!kQ2) load_q(Qreg, s1, Ln);  // the Q operand registers are free now
 #pragma unroll
         for (int sp = 0; sp < NSP; ++sp)
           if (2 * sp <= qmax) pv(sp);
@@ -556,7 +563,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
           scores(sp);
           pv(sp);
         }
-        load_q(s1, Ln);
+        if constexpr (!kQ2) load_q(Qreg, s1, Ln);
       }
       if constexpr (NB == 1) lds_barrier();  // this chunk's K, V and R^T are no longer read
       // store Y rows, 4 columns (8 bytes) per lane and block (rows past the
@@ -574,6 +581,15 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         }
       }
       lds_barrier();  // the next chunk's R^T, K and V are in LDS
+    };
+    for (int ci = 0; ci < nchunks; ci += 2) {
+      if constexpr (kQ2) {
+        chunk(ci, Qa, Qb);
+        if (ci + 1 < nchunks) chunk(ci + 1, Qb, Qa);
+      } else {
+        chunk(ci, Qa, Qa);
+        if (ci + 1 < nchunks) chunk(ci + 1, Qa, Qa);
+      }
     }
   }
 }
