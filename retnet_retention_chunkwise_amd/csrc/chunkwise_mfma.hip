@@ -36,6 +36,8 @@
 // chunk's last valid row, so rows past the end read as zero / are dropped
 // without branches.  Decay factors gamma^d come from log2(gamma) with
 // gamma^0 forced to 1.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -132,12 +134,14 @@ struct SegArgs {
 // kOut = true: the full kernel (outputs and state, 4 + 4 waves).
 // kOut = false: the state-only pass over segments 0..nseg-2 (4 state waves).
 // kZS = true: V is staged in LDS already scaled by zeta_t = gamma^(L-1-t), once
-// per element, and serves both the state update and the outputs.  The
-// outputs then use P' = (Q K^T .* causal mask) diag-scaled by gamma^(j-L+1)
-// per query row j, since gamma^(j-t) V_t = gamma^(j-L+1) zeta_t V_t.  The
-// factors stay within 2^+-100 when gamma^(CT-1) >= 2^-100 (the host checks
-// this for every head of the launch).  kZS = false keeps V unscaled and
-// applies zeta to the update's operand in registers (any gamma in [0, 1]).
+// per element, and serves both the state update and the outputs.  Since
+// gamma^(j-t) V_t = gamma^(j+1) gamma^(-L) zeta_t V_t, the outputs are
+//   O_j = gamma^(j+1) (Q R + ((Q K^T) .* causal mask) gamma^(-L) zeta V)_j,
+// with one scalar gamma^(-L) per chunk.  zeta >= gamma^(CT-1) and
+// gamma^(-L) <= gamma^(-CT) stay within about 2^+-102 when
+// gamma^(CT-1) >= 2^-100 (the host checks this for every head of the launch).
+// kZS = false keeps V unscaled and applies zeta to the update's operand in
+// registers (any gamma in [0, 1]).
 template <int CT, int DK, bool kOut, bool kZS>
 __global__ __attribute__((amdgpu_flat_work_group_size(kOut ? 512 : 256, kOut ? 512 : 256),
                           amdgpu_waves_per_eu(kOut ? 2 : 1, 2))) void
@@ -205,7 +209,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
           const int d = dbase + 16 * mb + 4 * g + i;
           Racc[mb][nb][i] = init != nullptr ? init[sbase + static_cast<long>(d) * dv + 16 * nb + c16] : 0.0f;
         }
-    auto write_rt = [&](int buf) {
+    auto write_rt = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int mb = 0; mb < F::RM; ++mb)
 #pragma unroll
@@ -225,43 +229,56 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     const int krow = KPR == 8 ? prow : st / KPR;
     const int kc8 = KPR == 8 ? (st & 7) : st % KPR;
     const int vc8 = st & 7;
-    u32x4 kreg[F::KPT];
-    u32x4 vreg[F::VPT];
+    // K/V staging registers.  With two LDS copies and zeta-staged V (whose
+    // update needs fewer registers) there are two register sets: chunk c+1
+    // waits in set c%2 and is loaded two chunks before it is written to LDS,
+    // which covers the latency of cold HBM reads.  Otherwise one set holds
+    // the chunk after next.
+    constexpr int NKV = (NB == 2 && kZS) ? 2 : 1;
+    u32x4 kreg[NKV][F::KPT];
+    u32x4 vreg[NKV][F::VPT];
     const uint32_t koff = static_cast<uint32_t>(krow * DK + 8 * kc8) * 2u;  // + r * KRR rows
     const uint32_t voff = static_cast<uint32_t>(prow) * vrow + 16u * vc8;   // + r * 32 rows
-    auto load_kv = [&](int s1, int Ln) {
+    // the register set is a compile-time constant (std::integral_constant), so
+    // the arrays are indexed statically whether or not the lambdas are inlined
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    auto load_kv = [&](auto set_c, int s1, int Ln) __attribute__((always_inline)) {
+      constexpr int set = decltype(set_c)::value;
       const rsrc_t rk = make_rsrc(kh + static_cast<long>(s1) * DK, static_cast<uint32_t>(Ln) * DK * 2u);
 #pragma unroll
-      for (int r = 0; r < F::KPT; ++r) kreg[r] = buffer_load16(rk, koff + static_cast<uint32_t>(r * KRR * DK * 2));
+      for (int r = 0; r < F::KPT; ++r)
+        kreg[set][r] = buffer_load16(rk, koff + static_cast<uint32_t>(r * KRR * DK * 2));
       const rsrc_t rv = make_rsrc(vh + static_cast<long>(s1) * dv,
                                   Ln > 0 ? static_cast<uint32_t>(Ln - 1) * vrow + kTN * 2u : 0u);
 #pragma unroll
-      for (int r = 0; r < F::VPT; ++r) vreg[r] = buffer_load16(rv, voff + 32u * vrow * r);
+      for (int r = 0; r < F::VPT; ++r) vreg[set][r] = buffer_load16(rv, voff + 32u * vrow * r);
     };
     // Ln: length of the chunk being staged (zeta of its rows when kZS)
-    auto store_kv = [&](int buf, int Ln) {
+    auto store_kv = [&](auto set_c, int buf, int Ln) __attribute__((always_inline)) {
+      constexpr int set = decltype(set_c)::value;
 #pragma unroll
       for (int r = 0; r < F::KPT; ++r)
-        *reinterpret_cast<u32x4*>(&Ks[buf][(krow + r * KRR) * F::KLD + 8 * kc8]) = kreg[r];
+        *reinterpret_cast<u32x4*>(&Ks[buf][(krow + r * KRR) * F::KLD + 8 * kc8]) = kreg[set][r];
 #pragma unroll
       for (int r = 0; r < F::VPT; ++r) {
         const int row = prow + 32 * r;
         if constexpr (kZS) {
           const float z = row < Ln ? gamma_pow(lg, Ln - 1 - row) : 0.0f;
-          const f32x8 vf = __builtin_convertvector(__builtin_bit_cast(bf16x8, vreg[r]), f32x8) * z;
+          const f32x8 vf = __builtin_convertvector(__builtin_bit_cast(bf16x8, vreg[set][r]), f32x8) * z;
           *reinterpret_cast<bf16x8*>(&Vs[buf][row * F::VLD + 8 * vc8]) = __builtin_convertvector(vf, bf16x8);
         } else {
-          *reinterpret_cast<u32x4*>(&Vs[buf][row * F::VLD + 8 * vc8]) = vreg[r];
+          *reinterpret_cast<u32x4*>(&Vs[buf][row * F::VLD + 8 * vc8]) = vreg[set][r];
         }
       }
     };
     // zeta*V for the one-copy layout: zeta_row = gamma^(L-1-row), 0 past the chunk end
-    auto store_vz = [&](int Ln) {
+    auto store_vz = [&](int Ln) __attribute__((always_inline)) {
 #pragma unroll
       for (int r = 0; r < F::VPT; ++r) {
         const int row = prow + 32 * r;
         const float z = row < Ln ? gamma_pow(lg, Ln - 1 - row) : 0.0f;
-        const f32x8 vf = __builtin_convertvector(__builtin_bit_cast(bf16x8, vreg[r]), f32x8) * z;
+        const f32x8 vf = __builtin_convertvector(__builtin_bit_cast(bf16x8, vreg[0][r]), f32x8) * z;
         *reinterpret_cast<bf16x8*>(&Vz[row * F::VLD + 8 * vc8]) = __builtin_convertvector(vf, bf16x8);
       }
     };
@@ -279,7 +296,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     // uses k-slot e of lane group g <-> token 32s + 8g + 2(e%4) + e/4 for both
     // operands: each transposing read then touches rows {0,2,..,14} or
     // {1,3,..,15} (+16), which the padded row strides place in disjoint banks.
-    auto update = [&](int buf, int L) {
+    auto update = [&](int buf, int L) __attribute__((always_inline)) {
       const float gL = L == C ? gamma_pow(lg, C) : gamma_pow(lg, L);
 #pragma unroll
       for (int mb = 0; mb < F::RM; ++mb)
@@ -290,7 +307,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       // registers of a full tile and read each step just before use.
       constexpr int PB = NB == 2 ? 2 : 1;
       bf16x8 zb[PB][4], ka[PB][F::RM];
-      auto read_step = [&](int s, int slot) {
+      auto read_step = [&](int s, int slot) __attribute__((always_inline)) {
         const uint16_t* vsrc = kVz ? Vz : Vs[buf];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
@@ -345,41 +362,54 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       }
     };
 
+    // length of the chunk starting at token s (0 past the segment end); loads
+    // of such empty chunks are issued anyway (they read zeros) so that the
+    // wait counts stay exact
+    auto clen = [&](int s) __attribute__((always_inline)) { return s < t_end ? min(C, t_end - s) : 0; };
     {
-      const int L0 = min(C, t_end - t_begin);
-      load_kv(t_begin, L0);
+      const int L0 = clen(t_begin);
+      load_kv(I0(), t_begin, L0);
       if constexpr (kOut) write_rt(0);
-      store_kv(0, L0);
+      store_kv(I0(), 0, L0);
       if constexpr (kVz) store_vz(L0);
-      if constexpr (NB == 2) {
-        const int s1 = t_begin + C;
-        load_kv(s1, s1 < t_end ? min(C, t_end - s1) : 0);  // chunk 1 into registers
-      }
+      if constexpr (NB == 2) load_kv(I0(), t_begin + C, clen(t_begin + C));            // chunk 1 into set 0
+      if constexpr (NKV == 2) load_kv(I1(), t_begin + 2 * C, clen(t_begin + 2 * C));  // chunk 2 into set 1
     }
     lds_barrier();  // chunk 0 staged, R_0 published
 
-    for (int ci = 0; ci < nchunks; ++ci) {
+    // one chunk with two LDS copies: chunk ci+1 waits in register set SET
+    // (ci%2 with two sets)
+    auto iter2 = [&](int ci, auto set_c) __attribute__((always_inline)) {
+      using SET = std::integral_constant<int, NKV == 2 ? decltype(set_c)::value : 0>;
       const int s0 = t_begin + ci * C;
       const int L = min(C, t_end - s0);
-      const int s1 = s0 + C;
-      const int Ln = s1 < t_end ? min(C, t_end - s1) : 0;
-      if constexpr (NB == 2) {
-        const int X = ci & 1;
-        update(X, L);
-        if constexpr (kOut) write_rt(X ^ 1);  // R_(i+1) into the other copy
-        if (Ln > 0) store_kv(X ^ 1, Ln);      // chunk i+1 (loaded during chunk i-1)
-        const int s2 = s1 + C;
-        load_kv(s2, s2 < t_end ? min(C, t_end - s2) : 0);  // chunk i+2 into registers
-        lds_barrier();
-      } else {
-        // next chunk's K/V, issued unconditionally (an empty buffer past the end
-        // reads zeros) so the wait counts stay exact; written after the barrier
-        load_kv(s1, Ln);
+      const int Ln = clen(s0 + C);
+      const int X = ci & 1;
+      update(X, L);
+      if constexpr (kOut) write_rt(X ^ 1);      // R_(i+1) into the other copy
+      if (Ln > 0) store_kv(SET(), X ^ 1, Ln);   // chunk i+1
+      const int sn = s0 + (NKV + 1) * C;        // chunk i+3 (two sets) or i+2 into the freed set
+      load_kv(SET(), sn, clen(sn));
+      lds_barrier();
+    };
+    if constexpr (NB == 2) {
+      for (int ci = 0; ci < nchunks; ci += 2) {
+        iter2(ci, I0());
+        if (ci + 1 < nchunks) iter2(ci + 1, I1());
+      }
+    } else {
+      for (int ci = 0; ci < nchunks; ++ci) {
+        const int s0 = t_begin + ci * C;
+        const int L = min(C, t_end - s0);
+        const int s1 = s0 + C;
+        const int Ln = clen(s1);
+        // next chunk's K/V, written after the barrier
+        load_kv(I0(), s1, Ln);
         update(0, L);
         lds_barrier();  // output waves are done with R^T, K and V of this chunk
         if constexpr (kOut) write_rt(0);
         if (Ln > 0) {
-          store_kv(0, Ln);
+          store_kv(I0(), 0, Ln);
           if constexpr (kVz) store_vz(Ln);
         }
         lds_barrier();  // R_(i+1) and the next chunk's K/V are in LDS
@@ -402,13 +432,13 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     }
   } else if constexpr (kOut) {
     // =========================== output waves ===========================
-    int qblk[F::NQ];
-    if constexpr (F::NQ == 2) {
-      qblk[0] = wr;
-      qblk[1] = 7 - wr;
-    } else {
-      qblk[0] = wr;
-    }
+    // One code path per output wave: its query blocks ({W} for 64-token tiles,
+    // {W, 7-W} for 128-token tiles, which balances the causal triangle) are
+    // compile-time constants, so the causal block structure needs no branches.
+    auto out_role = [&](auto w_c) __attribute__((always_inline)) {
+    constexpr int W = decltype(w_c)::value;
+    constexpr int QB1 = F::NQ == 2 ? 7 - W : W;
+    constexpr int QMAX = QB1 > W ? QB1 : W;  // last query block of the wave
     // Decay factors (positions are chunk-relative, so these do not depend on
     // the chunk).  Off-diagonal key block kb < qb:
     //   gamma^(j-t) = gamma^(16(qb-kb) + c16 - 4g - 3) * cst[t % 4],  cst[e] = gamma^(3-e)
@@ -428,11 +458,11 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     constexpr bool kQ2 = F::NQ == 1;
     typedef bf16x8 QTile[F::NQ][F::KS];
     QTile Qa, Qb;
-    auto load_q = [&](QTile& Qd, int s1, int Ln) {
+    auto load_q = [&](QTile& Qd, int s1, int Ln) __attribute__((always_inline)) {
       const rsrc_t rq = make_rsrc(qh + static_cast<long>(s1) * DK, static_cast<uint32_t>(Ln) * DK * 2u);
 #pragma unroll
       for (int qi = 0; qi < F::NQ; ++qi) {
-        const uint32_t rowoff = static_cast<uint32_t>(16 * qblk[qi] + c16) * DK * 2u + 16u * g;
+        const uint32_t rowoff = static_cast<uint32_t>(16 * (qi == 0 ? W : QB1) + c16) * DK * 2u + 16u * g;
 #pragma unroll
         for (int s = 0; s < F::KS; ++s) Qd[qi][s] = __builtin_bit_cast(bf16x8, buffer_load16(rq, rowoff + 64u * s));
       }
@@ -441,7 +471,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     lds_barrier();  // chunk 0 staged, R_0 published
 
     // one chunk with Q in Qreg; Qnext receives the next chunk's Q (kQ2)
-    auto chunk = [&](int ci, QTile& Qreg, QTile& Qnext) {
+    auto chunk = [&](int ci, QTile& Qreg, QTile& Qnext) __attribute__((always_inline)) {
       const int s0 = t_begin + ci * C;
       const int L = min(C, t_end - s0);
       const int s1 = s0 + C;
@@ -456,7 +486,36 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       // accumulates on top.  O^T[16nb + 4g + i][query c16] sits in lane
       // (g, c16): four consecutive value columns of one query row.
       f32x4 O[F::NQ][4];
-      {
+      // With one query block (64-token tiles) the cross term and the scores
+      // share one pass over d_k: each step's Q operand feeds 4 cross-term and
+      // up to 4 score products, whose LDS reads are issued a step ahead.
+      constexpr bool kMerged = F::NQ == 1;
+      f32x4 St[F::NQ][NSP][2];
+      if constexpr (kMerged) {
+        bf16x8 rb[2][4], kk[2][NSP][2];
+        auto rd = [&](int s, int slot) __attribute__((always_inline)) {
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) rb[slot][nb] = lds_read16(&Rx[(16 * nb + c16) * F::RLD + 32 * s + 8 * g]);
+#pragma unroll
+          for (int sp = 0; sp < NSP; ++sp)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              if (2 * sp + h <= W) kk[slot][sp][h] = lds_read16(&Kx[(32 * sp + 16 * h + c16) * F::KLD + 32 * s + 8 * g]);
+        };
+        rd(0, 0);
+#pragma unroll
+        for (int s = 0; s < F::KS; ++s) {
+          if (s + 1 < F::KS) rd(s + 1, (s + 1) & 1);
+          const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) O[0][nb] = mfma(rb[s & 1][nb], Qreg[0][s], s == 0 ? z4 : O[0][nb]);
+#pragma unroll
+          for (int sp = 0; sp < NSP; ++sp)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              if (2 * sp + h <= W) St[0][sp][h] = mfma(kk[s & 1][sp][h], Qreg[0][s], s == 0 ? z4 : St[0][sp][h]);
+        }
+      } else {
         bf16x8 rb[2][4];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) rb[0][nb] = lds_read16(&Rx[(16 * nb + c16) * F::RLD + 8 * g]);
@@ -474,26 +533,29 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
               O[qi][nb] = mfma(rb[s & 1][nb], Qreg[qi][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : O[qi][nb]);
         }
       }
-      float rowf[F::NQ];  // gamma^(j-L+1) for this lane's query row j (kZS)
+      // gamma^(j+1) of this lane's query rows j.  Without kZS it scales the
+      // cross term here; with kZS it is factored out of both terms,
+      //   O = gamma^(j+1) (Q R + (S .* mask) gamma^(-L) zeta V),
+      // and applied when O is converted for the store, so the cross-term and
+      // P V products accumulate without a pass over O in between.
+      float xi[F::NQ];
 #pragma unroll
       for (int qi = 0; qi < F::NQ; ++qi) {
-        const int j = 16 * qblk[qi] + c16;
-        const float xi = gamma_pow(lg, j + 1);
+        xi[qi] = gamma_pow(lg, 16 * (qi == 0 ? W : QB1) + c16 + 1);
+        if constexpr (!kZS) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) O[qi][nb] *= xi;
-        rowf[qi] = kZS ? exp2f(static_cast<float>(j - L + 1) * lg) : 1.0f;
+          for (int nb = 0; nb < 4; ++nb) O[qi][nb] *= xi[qi];
+        }
       }
+      const float ginvL = kZS ? exp2f(-static_cast<float>(L) * lg) : 1.0f;  // gamma^(-L)
 
       // intra-chunk term: key steps of 32 keys on or below the diagonal.  When
       // the scores of all key steps fit in registers (64-token tiles), every
       // S^T block is computed first so that the next chunk's Q loads can be
       // issued before the P V products; otherwise S^T and P V alternate per
       // key step and the Q loads follow.
-      const int qmax = F::NQ == 2 ? max(qblk[0], qblk[1]) : qblk[0];
       constexpr bool kAllScoresFirst = true;
-      constexpr int NSS = kAllScoresFirst ? NSP : 1;  // key steps whose scores are live at once
-      f32x4 St[F::NQ][NSS][2];
-      auto scores = [&](int sp) {
+      auto scores = [&](int sp) __attribute__((always_inline)) {
         const int slot = kAllScoresFirst ? sp : 0;
 #pragma unroll
         for (int s = 0; s < F::KS; ++s) {
@@ -501,14 +563,14 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
           const bf16x8 kb = lds_read16(&Kx[(32 * sp + 16 + c16) * F::KLD + 32 * s + 8 * g]);
 #pragma unroll
           for (int qi = 0; qi < F::NQ; ++qi) {
-            if (qblk[qi] >= 2 * sp)
+            if ((qi == 0 ? W : QB1) >= 2 * sp)
               St[qi][slot][0] = mfma(ka, Qreg[qi][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : St[qi][slot][0]);
-            if (qblk[qi] >= 2 * sp + 1)
+            if ((qi == 0 ? W : QB1) >= 2 * sp + 1)
               St[qi][slot][1] = mfma(kb, Qreg[qi][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : St[qi][slot][1]);
           }
         }
       };
-      auto pv = [&](int sp) {
+      auto pv = [&](int sp) __attribute__((always_inline)) {
         const int slot = kAllScoresFirst ? sp : 0;
         // V^T operands (keys 32sp+4g+e and 32sp+16+4g+e), shared by the wave's query blocks
         bf16x8 vb[4];
@@ -521,16 +583,16 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         }
 #pragma unroll
         for (int qi = 0; qi < F::NQ; ++qi) {
-          if (qblk[qi] < 2 * sp) continue;
+          if ((qi == 0 ? W : QB1) < 2 * sp) continue;
           f32x8 p;
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const int m = qblk[qi] - (2 * sp + h);  // wave-uniform
+            const int m = (qi == 0 ? W : QB1) - (2 * sp + h);  // wave-uniform
             if constexpr (kZS) {
-              // P' = S .* causal mask, times gamma^(j-L+1) of this lane's row
+              // P'' = (S .* causal mask) gamma^(-L)
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                p[4 * h + e] = (m > 0 || (m == 0 && 4 * g + e <= c16)) ? St[qi][slot][h][e] * rowf[qi] : 0.0f;
+                p[4 * h + e] = (m > 0 || (m == 0 && 4 * g + e <= c16)) ? St[qi][slot][h][e] * ginvL : 0.0f;
             } else {
               const float boff = m > 0 ? exp2f(static_cast<float>(16 * m + lane_off) * lg) : 0.0f;
 #pragma unroll
@@ -551,15 +613,15 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       if constexpr (kAllScoresFirst) {
 #pragma unroll
         for (int sp = 0; sp < NSP; ++sp)
-          if (2 * sp <= qmax) scores(sp);
+          if (!kMerged && 2 * sp <= QMAX) scores(sp);
         if constexpr (!kQ2) load_q(Qreg, s1, Ln);  // the Q operand registers are free now
 #pragma unroll
         for (int sp = 0; sp < NSP; ++sp)
-          if (2 * sp <= qmax) pv(sp);
+          if (2 * sp <= QMAX) pv(sp);
       } else {
 #pragma unroll
         for (int sp = 0; sp < NSP; ++sp) {
-          if (2 * sp > qmax) break;
+          if (2 * sp > QMAX) break;
           scores(sp);
           pv(sp);
         }
@@ -572,10 +634,10 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         const rsrc_t ry = make_rsrc(yh + static_cast<long>(s0) * dv, static_cast<uint32_t>(L - 1) * vrow + kTN * 2u);
 #pragma unroll
         for (int qi = 0; qi < F::NQ; ++qi) {
-          const uint32_t roff = static_cast<uint32_t>(16 * qblk[qi] + c16) * vrow + 8u * g;
+          const uint32_t roff = static_cast<uint32_t>(16 * (qi == 0 ? W : QB1) + c16) * vrow + 8u * g;
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb) {
-            const bf16x4 o = __builtin_convertvector(O[qi][nb], bf16x4);
+            const bf16x4 o = __builtin_convertvector(kZS ? O[qi][nb] * xi[qi] : O[qi][nb], bf16x4);
             buffer_store8(ry, roff + 32u * nb, __builtin_bit_cast(u32x2, o));
           }
         }
@@ -590,6 +652,13 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         chunk(ci, Qa, Qa);
         if (ci + 1 < nchunks) chunk(ci + 1, Qa, Qa);
       }
+    }
+    };
+    switch (wr) {
+      case 0: out_role(std::integral_constant<int, 0>()); break;
+      case 1: out_role(std::integral_constant<int, 1>()); break;
+      case 2: out_role(std::integral_constant<int, 2>()); break;
+      default: out_role(std::integral_constant<int, 3>()); break;
     }
   }
 }
