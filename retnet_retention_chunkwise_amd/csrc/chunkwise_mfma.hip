@@ -491,6 +491,25 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       // up to 4 score products, whose LDS reads are issued a step ahead.
       constexpr bool kMerged = F::NQ == 1;
       f32x4 St[F::NQ][NSP][2];
+      // V^T operands of key step sp (keys 32sp+4g+e and 32sp+16+4g+e), in
+      // the key order of the S^T accumulators
+      auto read_v = [&](int sp, bf16x8 (&vb)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int col = 16 * nb + 4 * (c16 & 3);
+          const s16x4 lo = lds_read_tr(&Vx[(32 * sp + 4 * g + (c16 >> 2)) * F::VLD + col]);
+          const s16x4 hi = lds_read_tr(&Vx[(32 * sp + 16 + 4 * g + (c16 >> 2)) * F::VLD + col]);
+          vb[nb] = join(lo, hi);
+        }
+      };
+      // 64-token tiles: the V operands are read before the d_k pass, so that
+      // they arrive while it runs
+      bf16x8 vpre[kMerged ? NSP : 1][4];
+      if constexpr (kMerged) {
+#pragma unroll
+        for (int sp = 0; sp < NSP; ++sp)
+          if (2 * sp <= W) read_v(sp, vpre[sp]);
+      }
       if constexpr (kMerged) {
         bf16x8 rb[2][4], kk[2][NSP][2];
         auto rd = [&](int s, int slot) __attribute__((always_inline)) {
@@ -572,14 +591,12 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       };
       auto pv = [&](int sp) __attribute__((always_inline)) {
         const int slot = kAllScoresFirst ? sp : 0;
-        // V^T operands (keys 32sp+4g+e and 32sp+16+4g+e), shared by the wave's query blocks
         bf16x8 vb[4];
+        if constexpr (kMerged) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int col = 16 * nb + 4 * (c16 & 3);
-          const s16x4 lo = lds_read_tr(&Vx[(32 * sp + 4 * g + (c16 >> 2)) * F::VLD + col]);
-          const s16x4 hi = lds_read_tr(&Vx[(32 * sp + 16 + 4 * g + (c16 >> 2)) * F::VLD + col]);
-          vb[nb] = join(lo, hi);
+          for (int nb = 0; nb < 4; ++nb) vb[nb] = vpre[sp][nb];
+        } else {
+          read_v(sp, vb);
         }
 #pragma unroll
         for (int qi = 0; qi < F::NQ; ++qi) {
