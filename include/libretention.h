@@ -85,7 +85,10 @@ ret_status retention_parallel_fwd(const void* q, const void* k, const void* v, c
  *               May alias state_in exactly (in-place continuation).
  *   y         : written, [B,H,T,dv] in dt; must not alias an input.
  *   workspace : device scratch of at least retention_chunkwise_workspace_bytes()
- *               bytes for the same arguments (may be NULL when that is 0).
+ *               bytes for the same arguments (may be NULL when that is 0), owned
+ *               by the caller, 16-byte aligned, overlapping no other argument;
+ *               its contents on entry are ignored and on return undefined.  A
+ *               missing or short workspace is RET_ERR_INVALID_ARG.
  * T = 0 is valid: y is untouched and state_out receives state_in (or zeros).
  */
 ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, const float* gamma,
@@ -94,7 +97,11 @@ ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, 
                                    size_t workspace_bytes, void* stream);
 
 /* Workspace size for retention_chunkwise_fwd with these arguments (0 when the
- * chosen kernel needs none).  Returns (size_t)-1 for arguments the call would reject. */
+ * chosen kernel needs none).  bf16 calls whose (batch, head, 64-column tile)
+ * count is below the device's 256 compute units and whose sequence has at
+ * least 16 chunks run in sequence segments; they need one fp32 state slot per
+ * segment: nseg * B * H * dk * dv * 4 bytes.  A pure function of the sizes.
+ * Returns (size_t)-1 for arguments the call would reject. */
 size_t retention_chunkwise_workspace_bytes(int B, int H, int T, int dk, int dv, int C, ret_dtype dt);
 
 /*
