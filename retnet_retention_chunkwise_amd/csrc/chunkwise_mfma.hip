@@ -489,7 +489,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       // With one query block (64-token tiles) the cross term and the scores
       // share one pass over d_k: each step's Q operand feeds 4 cross-term and
       // up to 4 score products, whose LDS reads are issued a step ahead.
-      constexpr bool kMerged = F::NQ == 1;
+      constexpr bool kMerged = true;
       f32x4 St[F::NQ][NSP][2];
       // V^T operands of key step sp (keys 32sp+4g+e and 32sp+16+4g+e), in
       // the key order of the S^T accumulators
@@ -503,23 +503,23 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         }
       };
       // 64-token tiles: the V operands are read before the d_k pass, so that
-      // they arrive while it runs
-      bf16x8 vpre[kMerged ? NSP : 1][4];
-      if constexpr (kMerged) {
+      // they arrive while it runs (128-token tiles read them per key step)
+      constexpr bool kVpre = F::NQ == 1;
+      bf16x8 vpre[kVpre ? NSP : 1][4];
+      if constexpr (kVpre) {
 #pragma unroll
         for (int sp = 0; sp < NSP; ++sp)
           if (2 * sp <= W) read_v(sp, vpre[sp]);
       }
       if constexpr (kMerged) {
-        bf16x8 rb[2][4], kk[2][NSP][2];
+        // key blocks 0..QMAX are read once per step and serve both query blocks
+        constexpr int KB = QMAX + 1;
+        bf16x8 rb[2][4], kk[2][KB];
         auto rd = [&](int s, int slot) __attribute__((always_inline)) {
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb) rb[slot][nb] = lds_read16(&Rx[(16 * nb + c16) * F::RLD + 32 * s + 8 * g]);
 #pragma unroll
-          for (int sp = 0; sp < NSP; ++sp)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-              if (2 * sp + h <= W) kk[slot][sp][h] = lds_read16(&Kx[(32 * sp + 16 * h + c16) * F::KLD + 32 * s + 8 * g]);
+          for (int kb = 0; kb < KB; ++kb) kk[slot][kb] = lds_read16(&Kx[(16 * kb + c16) * F::KLD + 32 * s + 8 * g]);
         };
         rd(0, 0);
 #pragma unroll
@@ -527,12 +527,15 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
           if (s + 1 < F::KS) rd(s + 1, (s + 1) & 1);
           const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) O[0][nb] = mfma(rb[s & 1][nb], Qreg[0][s], s == 0 ? z4 : O[0][nb]);
+          for (int qi = 0; qi < F::NQ; ++qi)
 #pragma unroll
-          for (int sp = 0; sp < NSP; ++sp)
+            for (int nb = 0; nb < 4; ++nb) O[qi][nb] = mfma(rb[s & 1][nb], Qreg[qi][s], s == 0 ? z4 : O[qi][nb]);
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-              if (2 * sp + h <= W) St[0][sp][h] = mfma(kk[s & 1][sp][h], Qreg[0][s], s == 0 ? z4 : St[0][sp][h]);
+          for (int qi = 0; qi < F::NQ; ++qi)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+              if (kb <= (qi == 0 ? W : QB1))
+                St[qi][kb / 2][kb % 2] = mfma(kk[s & 1][kb], Qreg[qi][s], s == 0 ? z4 : St[qi][kb / 2][kb % 2]);
         }
       } else {
         bf16x8 rb[2][4];
@@ -592,7 +595,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       auto pv = [&](int sp) __attribute__((always_inline)) {
         const int slot = kAllScoresFirst ? sp : 0;
         bf16x8 vb[4];
-        if constexpr (kMerged) {
+        if constexpr (kVpre) {
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb) vb[nb] = vpre[sp][nb];
         } else {
