@@ -7,31 +7,33 @@
 //   Y_[i]   = ((Q_[i] K_[i]^T) .* D_L) V_[i] + diag(gamma^(j+1)) Q_[i] R_i
 //   R_(i+1) = gamma^L R_i + K_[i]^T (diag(gamma^(L-1-j)) V_[i])
 //
-// Work decomposition.  A workgroup owns one (batch, head, tile of 64 value
-// columns) and walks the chunks of the sequence in order; the 8 column tiles
-// of a head are placed on one XCD so that their shared Q/K reads hit one L2.
-// The workgroup has 8 waves in two roles, one of each per SIMD (waves w and
-// w+4 share a SIMD), so that each role's memory and LDS latencies are covered
-// by the other role's instructions:
-//   * output waves 0..3 own 16-row query blocks ({w, 7-w} for 128-token
-//     chunks, which balances the causal triangle; {w} for 64-token chunks).
-//     Their Q rows are loaded from global memory straight into MFMA operand
-//     registers and serve both S^T = K Q^T and the cross term Q R.  S^T stays
-//     in registers: its accumulator layout is, up to a permutation of the key
-//     index, the A-operand layout that P = S .* D needs for P V, so the decay
-//     mask is applied in registers and P never touches LDS.  V is read with
-//     the same key permutation through ds_read_b64_tr_b16, the gfx950
-//     transposing LDS load.  The cross term reads R^T (bf16) from LDS.
+// Work decomposition.  A workgroup owns one (segment, batch, head, tile of 64
+// value columns) and walks the chunks of its segment in order; the 8 column
+// tiles of a head are placed on one XCD so that their shared Q/K reads hit
+// one L2.  The workgroup has 8 waves in two roles, one of each per SIMD
+// (waves w and w+4 share a SIMD):
+//   * output waves 0..3 own 16-row query blocks ({w} for 64-token tiles,
+//     {w, 7-w} for 128-token tiles, which balances the causal triangle), each
+//     with a code path specialised at compile time.  Their Q rows are loaded
+//     from global memory straight into MFMA operand registers.  One pass over
+//     d_k computes the cross term O^T = R_i^T Q^T (R^T from LDS) and the
+//     scores S^T = K Q^T of the key blocks up to the diagonal.  S^T stays in
+//     registers: its accumulator layout is, up to a permutation of the key
+//     index, the operand layout that P needs for P V, so P is formed in
+//     registers and never touches LDS; V^T is read with the same key
+//     permutation through ds_read_b64_tr_b16, the gfx950 transposing LDS load.
+//     O^T is accumulated, so each lane holds 4 consecutive columns of one
+//     query row for the Y stores.
 //   * state waves 4..7 own d_k/4 rows of the fp32 state tile R[d_k x 64],
-//     kept in MFMA accumulators for the whole sequence.  They run the update
-//     R <- gamma^L R + K^T (zeta V) (K^T and V through the transposing load,
-//     zeta_j = gamma^(L-1-j) applied in registers), publish R^T to LDS, and
-//     stage the next chunk's K and V tiles (global loads into registers a
-//     chunk ahead, LDS writes after the update).
-// 64-token chunks keep two copies of K, V and R^T in LDS, so staging chunk
-// i+1 overlaps the outputs of chunk i and one barrier per chunk suffices;
-// 128-token chunks keep one copy: [outputs | update] barrier [R^T and next
-// K/V written] barrier.
+//     kept in MFMA accumulators for the whole segment.  They run the update
+//     R <- gamma^L R + K^T (zeta V) (K^T and V through the transposing load),
+//     publish R^T to LDS, and stage the K and V tiles of later chunks (global
+//     loads into registers one or two chunks ahead, LDS writes after the
+//     update).
+// 64-token tiles keep two copies of K, V and R^T in LDS, so staging chunk i+1
+// overlaps the outputs of chunk i and one barrier per chunk suffices;
+// 128-token tiles with d_k = 256 keep one copy: [outputs | update] barrier
+// [R^T and next K/V written] barrier.  The barriers fence LDS only.
 // Every global access goes through a buffer resource that ends at the
 // chunk's last valid row, so rows past the end read as zero / are dropped
 // without branches.  Decay factors gamma^d come from log2(gamma) with
@@ -454,7 +456,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     const int lane_off = c16 - 4 * g - 3;
     // Q operand registers.  With one query block per wave there is room for
     // two copies: the next chunk's Q is loaded at the start of a chunk, a
-    // whole chunk ahead of its use; otherwise it is loaded after the scores.
+    // whole chunk ahead of its use; otherwise it is loaded after the d_k pass.
     constexpr bool kQ2 = F::NQ == 1;
     typedef bf16x8 QTile[F::NQ][F::KS];
     QTile Qa, Qb;
@@ -482,14 +484,14 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       const uint16_t* Rx = Rt[X];
       if constexpr (kQ2) load_q(Qnext, s1, Ln);
 
-      // cross-chunk term first: O^T = (R_i^T Q^T) diag(gamma^(j+1)), then V^T P^T
+      // cross-chunk term O^T = (R_i^T Q^T) diag(gamma^(j+1)); V^T P^T
       // accumulates on top.  O^T[16nb + 4g + i][query c16] sits in lane
       // (g, c16): four consecutive value columns of one query row.
       f32x4 O[F::NQ][4];
-      // With one query block (64-token tiles) the cross term and the scores
-      // share one pass over d_k: each step's Q operand feeds 4 cross-term and
-      // up to 4 score products, whose LDS reads are issued a step ahead.
-      constexpr bool kMerged = true;
+      // The cross term and the scores share one pass over d_k: each step's Q
+      // operand feeds the cross-term products (4 per query block) and the
+      // score products of the key blocks up to the diagonal; the LDS reads
+      // of a step are issued one step ahead.
       f32x4 St[F::NQ][NSP][2];
       // V^T operands of key step sp (keys 32sp+4g+e and 32sp+16+4g+e), in
       // the key order of the S^T accumulators
@@ -511,7 +513,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         for (int sp = 0; sp < NSP; ++sp)
           if (2 * sp <= W) read_v(sp, vpre[sp]);
       }
-      if constexpr (kMerged) {
+      {
         // key blocks 0..QMAX are read once per step and serve both query blocks
         constexpr int KB = QMAX + 1;
         bf16x8 rb[2][4], kk[2][KB];
@@ -537,23 +539,6 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
               if (kb <= (qi == 0 ? W : QB1))
                 St[qi][kb / 2][kb % 2] = mfma(kk[s & 1][kb], Qreg[qi][s], s == 0 ? z4 : St[qi][kb / 2][kb % 2]);
         }
-      } else {
-        bf16x8 rb[2][4];
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) rb[0][nb] = lds_read16(&Rx[(16 * nb + c16) * F::RLD + 8 * g]);
-#pragma unroll
-        for (int s = 0; s < F::KS; ++s) {
-          if (s + 1 < F::KS) {
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-              rb[(s + 1) & 1][nb] = lds_read16(&Rx[(16 * nb + c16) * F::RLD + 32 * (s + 1) + 8 * g]);
-          }
-#pragma unroll
-          for (int qi = 0; qi < F::NQ; ++qi)
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-              O[qi][nb] = mfma(rb[s & 1][nb], Qreg[qi][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : O[qi][nb]);
-        }
       }
       // gamma^(j+1) of this lane's query rows j.  Without kZS it scales the
       // cross term here; with kZS it is factored out of both terms,
@@ -571,29 +556,9 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       }
       const float ginvL = kZS ? exp2f(-static_cast<float>(L) * lg) : 1.0f;  // gamma^(-L)
 
-      // intra-chunk term: key steps of 32 keys on or below the diagonal.  When
-      // the scores of all key steps fit in registers (64-token tiles), every
-      // S^T block is computed first so that the next chunk's Q loads can be
-      // issued before the P V products; otherwise S^T and P V alternate per
-      // key step and the Q loads follow.
-      constexpr bool kAllScoresFirst = true;
-      auto scores = [&](int sp) __attribute__((always_inline)) {
-        const int slot = kAllScoresFirst ? sp : 0;
-#pragma unroll
-        for (int s = 0; s < F::KS; ++s) {
-          const bf16x8 ka = lds_read16(&Kx[(32 * sp + c16) * F::KLD + 32 * s + 8 * g]);
-          const bf16x8 kb = lds_read16(&Kx[(32 * sp + 16 + c16) * F::KLD + 32 * s + 8 * g]);
-#pragma unroll
-          for (int qi = 0; qi < F::NQ; ++qi) {
-            if ((qi == 0 ? W : QB1) >= 2 * sp)
-              St[qi][slot][0] = mfma(ka, Qreg[qi][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : St[qi][slot][0]);
-            if ((qi == 0 ? W : QB1) >= 2 * sp + 1)
-              St[qi][slot][1] = mfma(kb, Qreg[qi][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : St[qi][slot][1]);
-          }
-        }
-      };
+      // intra-chunk term: P V per key step of 32 keys on or below the diagonal
       auto pv = [&](int sp) __attribute__((always_inline)) {
-        const int slot = kAllScoresFirst ? sp : 0;
+        const int slot = sp;
         bf16x8 vb[4];
         if constexpr (kVpre) {
 #pragma unroll
@@ -630,23 +595,10 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
           for (int nb = 0; nb < 4; ++nb) O[qi][nb] = mfma(vb[nb], pa, O[qi][nb]);
         }
       };
-      if constexpr (kAllScoresFirst) {
+      if constexpr (!kQ2) load_q(Qreg, s1, Ln);  // the Q operand registers are free now
 #pragma unroll
-        for (int sp = 0; sp < NSP; ++sp)
-          if (!kMerged && 2 * sp <= QMAX) scores(sp);
-        if constexpr (!kQ2) load_q(Qreg, s1, Ln);  // the Q operand registers are free now
-#pragma unroll
-        for (int sp = 0; sp < NSP; ++sp)
-          if (2 * sp <= QMAX) pv(sp);
-      } else {
-#pragma unroll
-        for (int sp = 0; sp < NSP; ++sp) {
-          if (2 * sp > QMAX) break;
-          scores(sp);
-          pv(sp);
-        }
-        if constexpr (!kQ2) load_q(Qreg, s1, Ln);
-      }
+      for (int sp = 0; sp < NSP; ++sp)
+        if (2 * sp <= QMAX) pv(sp);
       if constexpr (NB == 1) lds_barrier();  // this chunk's K, V and R^T are no longer read
       // store Y rows, 4 columns (8 bytes) per lane and block (rows past the
       // chunk end fall outside the buffer and are dropped)
