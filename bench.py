@@ -13,14 +13,16 @@ The recurrent decode step (retention_recurrent_step, batch 128, H=16, fp32
 256x512 state per head, 1000 chained steps) is measured in the same run and
 reported in the "decode" object.
 
-Prints ONE JSON line.  The roofline of the chunkwise kernel uses algorithmic
-HBM bytes (bf16 Q, K, V in and Y out: 3072 bytes per head-token) over the
-kernel's average duration measured with HIP events on the launch stream.
+Prints ONE JSON line.  "value" is whole-job throughput over the timed loop.
+The roofline of the chunkwise kernel uses algorithmic HBM bytes (bf16 Q, K, V
+in and Y out: 3072 bytes per head-token) over the kernel's median launch
+duration, each launch bracketed by its own HIP event pair on the launch stream.
 """
 import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -59,6 +61,17 @@ def load_traffic(name, kernel_src):
         return float(rec["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 def cpu_baseline_chunkwise(wl, sample_B, sample_T):
@@ -156,7 +169,7 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
-    kernel_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    kernel_ms = statistics.median(a.elapsed_time(b) for a, b in ev)  # median launch duration
     tokens = wl.B * wl.T
     value = tokens / (ms_per_step * 1e-3)
     head_tokens = wl.B * wl.H * wl.T
@@ -190,7 +203,7 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     dec_ms = e0.elapsed_time(e1)
-    dec_kernel_us = sum(a.elapsed_time(b) for a, b in dev_ev) * 1e3 / args.decode_steps
+    dec_kernel_us = statistics.median(a.elapsed_time(b) for a, b in dev_ev) * 1e3
     dec_us_step = dec_ms * 1e3 / args.decode_steps
     state_bytes = dw.B * dw.H * dw.dk * dw.dv * 4
     dec_bytes = 2 * state_bytes + dw.B * dw.H * (2 * dw.dk + 2 * dw.dk + 2 * dw.dv + 2 * dw.dv)
@@ -248,7 +261,8 @@ def main():
         out["cpu_baseline"] = {
             "value": v_cpu, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"fp64 recurrent-form oracle on {sample_B} of {wl.B} batch elements x all {wl.H} heads x "
-                      f"{sample_T} of {wl.T} tokens of the layer1p3b workload: {dt:.1f} s",
+                      f"{sample_T} of {wl.T} tokens of the layer1p3b workload: {dt:.1f} s on {cores} threads "
+                      f"of {host_cpu_model()}",
         }
         dsteps = int(os.environ.get("RET_CPU_DECODE_STEPS", "64"))
         dbatch = int(os.environ.get("RET_CPU_DECODE_BATCH", "16"))
@@ -256,7 +270,7 @@ def main():
         out["decode"]["cpu_baseline"] = {
             "value": v_dec, "unit": "steps/s", "cores": cores, "kind": "oracle",
             "sample": f"fp64 oracle decode steps, {dbatch} of {dw.B} sequences x {dw.H} heads, {dsteps} steps "
-                      f"({ddt:.1f} s), scaled to the full batch",
+                      f"({ddt:.1f} s on {cores} threads of {host_cpu_model()}), scaled to the full batch",
         }
     print(json.dumps(out), flush=True)
 
