@@ -194,23 +194,52 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const int t_end = min(Tn, t_begin + sg.seg_len);
   const int nchunks = (t_end - t_begin + C - 1) / C;
 
+  // fp32 state tile in and out.  init: state_in (one segment), the scanned
+  // slot of this segment, or zero (state-only pass); fin: state_out (last
+  // segment) or, in the state-only pass, the slot of the next segment.  The
+  // [d_k x 64] tile moves through LDS (the K buffers, before the first chunk is
+  // staged and after the last one is read), so that global accesses are whole
+  // 256-byte rows; SRN rounds of SRR rows, two barriers per round in every wave.
+  const float* init = !kOut ? nullptr : (sg.nseg > 1 ? sg.ws + seg * sg.ws_stride : state_in);
+  float* fin = kOut ? (seg == sg.nseg - 1 ? state_out : nullptr) : sg.ws + (seg + 1) * sg.ws_stride;
+  constexpr int SLD = kTN + 4;                 // fp32 row stride in LDS
+  constexpr int SRR = DK < 128 ? DK : 128;     // rows per round
+  constexpr int SRN = DK / SRR;                // rounds
+  static_assert(SRR * SLD * 4 <= NB * CT * F::KLD * 2, "state staging does not fit the K buffers");
+  float* const Sst = reinterpret_cast<float*>(&Ks[0][0]);
+
   if (!kOut || w >= 4) {
     // =========================== state waves ===========================
     const int st = kOut ? tid - 256 : tid;  // staging thread index 0..255
     const int dbase = wr * (DK / 4);
-    // initial state: state_in (one segment), the scanned slot of this segment,
-    // or zero (state-only pass)
-    const float* init = !kOut ? nullptr : (sg.nseg > 1 ? sg.ws + seg * sg.ws_stride : state_in);
     f32x4 Racc[F::RM][4];
 #pragma unroll
     for (int mb = 0; mb < F::RM; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < 4; ++nb) Racc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (init != nullptr) {
+      for (int rr = 0; rr < SRN; ++rr) {
+        const int r0 = rr * SRR;
+        // 16 lanes per 256-byte row, 16 rows per pass of the 256 staging threads
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = dbase + 16 * mb + 4 * g + i;
-          Racc[mb][nb][i] = init != nullptr ? init[sbase + static_cast<long>(d) * dv + 16 * nb + c16] : 0.0f;
+        for (int p = 0; p < SRR / 16; ++p) {
+          const int row = 16 * p + (st >> 4);
+          *reinterpret_cast<u32x4*>(&Sst[row * SLD + 4 * (st & 15)]) =
+              *reinterpret_cast<const u32x4*>(&init[sbase + static_cast<long>(r0 + row) * dv + 4 * (st & 15)]);
         }
+        lds_barrier();
+#pragma unroll
+        for (int mb = 0; mb < F::RM; ++mb) {
+          const int d0 = dbase + 16 * mb;  // wave-uniform: the block lies in one round
+          if (d0 < r0 || d0 >= r0 + SRR) continue;
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Racc[mb][nb][i] = Sst[(d0 - r0 + 4 * g + i) * SLD + 16 * nb + c16];
+        }
+        lds_barrier();
+      }
+    }
     auto write_rt = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int mb = 0; mb < F::RM; ++mb)
@@ -418,22 +447,34 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       }
     }
 
-    // final state: state_out (last segment) or, in the state-only pass, the
-    // slot of the next segment
-    float* fin = kOut ? (seg == sg.nseg - 1 ? state_out : nullptr) : sg.ws + (seg + 1) * sg.ws_stride;
+    // final state (all K reads ended with the last chunk's barrier)
     if (fin != nullptr) {
+      for (int rr = 0; rr < SRN; ++rr) {
+        const int r0 = rr * SRR;
 #pragma unroll
-      for (int mb = 0; mb < F::RM; ++mb)
+        for (int mb = 0; mb < F::RM; ++mb) {
+          const int d0 = dbase + 16 * mb;
+          if (d0 < r0 || d0 >= r0 + SRR) continue;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+          for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int d = dbase + 16 * mb + 4 * g + i;
-            fin[sbase + static_cast<long>(d) * dv + 16 * nb + c16] = Racc[mb][nb][i];
-          }
+            for (int i = 0; i < 4; ++i) Sst[(d0 - r0 + 4 * g + i) * SLD + 16 * nb + c16] = Racc[mb][nb][i];
+        }
+        lds_barrier();
+#pragma unroll
+        for (int p = 0; p < SRR / 16; ++p) {
+          const int row = 16 * p + (st >> 4);
+          *reinterpret_cast<u32x4*>(&fin[sbase + static_cast<long>(r0 + row) * dv + 4 * (st & 15)]) =
+              *reinterpret_cast<const u32x4*>(&Sst[row * SLD + 4 * (st & 15)]);
+        }
+        lds_barrier();
+      }
     }
   } else if constexpr (kOut) {
     // =========================== output waves ===========================
+    // (the state tile's staging rounds: the same barriers as the state waves)
+    if (init != nullptr)
+      for (int rr = 0; rr < 2 * SRN; ++rr) lds_barrier();
     // One code path per output wave: its query blocks ({W} for 64-token tiles,
     // {W, 7-W} for 128-token tiles, which balances the causal triangle) are
     // compile-time constants, so the causal block structure needs no branches.
@@ -632,6 +673,8 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       case 2: out_role(std::integral_constant<int, 2>()); break;
       default: out_role(std::integral_constant<int, 3>()); break;
     }
+    if (fin != nullptr)
+      for (int rr = 0; rr < 2 * SRN; ++rr) lds_barrier();
   }
 }
 

@@ -181,6 +181,55 @@ def test_segmented_handoff_in_place_and_explicit_workspace():
     check("segmented split state", st, s_ref, 2e-2)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_prefill_decode_continuation(dt):
+    """Inference use of the three forms on one sequence: a chunkwise prefill of
+    300 tokens, 5 recurrent decode steps, then chunkwise continuations of 16
+    and 1 new tokens from the carried state (C = 16 and 1), against the oracle
+    on the concatenated 322 tokens."""
+    B, H, dk, dv = 2, 4, 64, 128
+    T0, nd, T1, T2 = 300, 5, 16, 1
+    T = T0 + nd + T1 + T2
+    say(f"prefill -> decode -> continuation, {dt}")
+    gs = [0.999, 0.99, 0.95, 0.8]
+    q, k, v, s0 = make_inputs(B, H, T, dk, dv, dt, seed=8, with_state=True)
+    y_ref, s_ref = oracle.recurrent(q, k, v, torch.tensor(gs, dtype=torch.float32), s0)
+    qd, kd, vd, sd = to_dev(q, k, v, s0)
+    st = sd.clone()
+    parts = []
+    y, _ = ret.chunkwise_fwd(qd[:, :, :T0].contiguous(), kd[:, :, :T0].contiguous(), vd[:, :, :T0].contiguous(), gs, 64,
+                             state_in=st, state_out=st)
+    parts.append(y)
+    for n in range(T0, T0 + nd):
+        parts.append(ret.recurrent_step(qd[:, :, n].contiguous(), kd[:, :, n].contiguous(), vd[:, :, n].contiguous(),
+                                        gs, st).unsqueeze(2))
+    a = T0 + nd
+    for Tn, C in ((T1, 16), (T2, 1)):
+        y, _ = ret.chunkwise_fwd(qd[:, :, a:a + Tn].contiguous(), kd[:, :, a:a + Tn].contiguous(),
+                                 vd[:, :, a:a + Tn].contiguous(), gs, C, state_in=st, state_out=st)
+        parts.append(y)
+        a += Tn
+    torch.cuda.synchronize()
+    check("continued y", torch.cat(parts, dim=2), y_ref, tol(q.dtype))
+    check("continued state", st, s_ref, tol(q.dtype))
+
+
+@pytest.mark.parametrize("Tn,C", [(1, 1), (7, 4), (16, 16), (64, 64), (100, 32)])
+def test_multi_token_decode_from_state(Tn, C):
+    """Chunkwise continuation of a batch of decode streams: Tn new tokens per
+    stream from a carried fp32 state (the decode workload's head shapes)."""
+    B, H, dk, dv = 8, 4, 256, 512
+    say(f"multi-token decode Tn={Tn} C={C}")
+    gs = gammas_for(H, 0.9)
+    q, k, v, s0 = make_inputs(B, H, Tn, dk, dv, "bf16", seed=9, with_state=True)
+    y_ref, s_ref = oracle.recurrent(q, k, v, torch.tensor(gs, dtype=torch.float32), s0)
+    qd, kd, vd, sd = to_dev(q, k, v, s0)
+    y, s = ret.chunkwise_fwd(qd, kd, vd, gs, C, state_in=sd)
+    torch.cuda.synchronize()
+    check("y", y, y_ref, 2e-2)
+    check("state", s, s_ref, 2e-2)
+
+
 def test_empty_sequence_copies_state():
     say("T = 0")
     B, H, dk, dv = 1, 2, 16, 32
