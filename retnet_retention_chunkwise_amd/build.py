@@ -28,6 +28,7 @@ SOURCES = [
     "chunkwise_generic.hip",
     "chunkwise_mfma.hip",
     "state_copy.hip",
+    "short_chunk.hip",
 ]
 
 ARCH = "gfx950"

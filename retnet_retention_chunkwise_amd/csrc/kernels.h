@@ -49,6 +49,14 @@ hipError_t launch_chunkwise_mfma(const void* q, const void* k, const void* v, co
                                  float* state_out, void* y, int B, int H, int T, int dk, int dv, int C,
                                  const ChunkSegments& segs, float* ws, const HeadGroup& g, hipStream_t s);
 
+// Streaming chunkwise kernel for a short block of tokens from a carried state
+// (1 <= T <= kShortChunkMaxT, fp32 or bf16 inputs, any supported dk and dv):
+// the whole block is one chunk, and the state is read and written once.
+constexpr int kShortChunkMaxT = 16;
+hipError_t launch_short_chunk(const void* q, const void* k, const void* v, const float* state_in, float* state_out,
+                              void* y, int B, int H, int T, int dk, int dv, int dt, const HeadGroup& g,
+                              hipStream_t s);
+
 // Copies state_in (or zeros when null) into state_out: the T = 0 case.
 hipError_t launch_state_copy(const float* state_in, float* state_out, size_t n, hipStream_t s);
 

@@ -162,3 +162,10 @@ def test_host_dispatch_of_every_parity_shape_without_a_device(lib):
         st = lib.retention_chunkwise_fwd(q, k, v, gam(*([0.5] * H)), None, None, y, B, H, T, dk, dv, C, d,
                                          w if need else None, need, None)
         assert st == 3, (B, H, T, dk, dv, C, dt, _lib.last_error())
+    for (B, H, T, dk, dv, dt, _, _, _) in parity.SHORT_CASES:
+        d = 1 if dt == "bf16" else 0
+        assert lib.retention_chunkwise_workspace_bytes(B, H, T, dk, dv, 64, d) == 0
+        q, k, v, y = (ctypes.c_void_p(a << 36) for a in (1, 2, 3, 4))
+        st = lib.retention_chunkwise_fwd(q, k, v, gam(*([0.5] * H)), None, None, y, B, H, T, dk, dv, 64, d, None, 0,
+                                         None)
+        assert st == 3, (B, H, T, dk, dv, dt, _lib.last_error())

@@ -107,6 +107,51 @@ def test_chunkwise_vs_oracle(B, H, T, dk, dv, C, dt, with_state, gs):
     check("state_out", s, s_ref, bound)
 
 
+# ------------------------------------- short blocks (T <= 16): streaming kernel
+SHORT_CASES = [
+    # B, H, T, dk, dv, dtype, state_in, state_out ("new" / "inplace" / None), gammas
+    (2, 3, 1, 64, 128, "f32", True, "new", [0.0, 0.9, 1.0]),
+    (1, 2, 2, 7, 5, "f32", True, "inplace", [0.5, 0.99]),
+    (2, 2, 3, 33, 300, "f32", False, "new", [0.8, 1.0]),
+    (1, 3, 4, 256, 512, "f32", True, None, [0.3, 0.7, 0.999]),
+    (2, 2, 5, 48, 260, "f32", True, "inplace", [0.0, 0.6]),
+    (1, 2, 8, 128, 37, "f32", True, "new", [0.95, 0.5]),
+    (2, 2, 9, 16, 64, "f32", False, None, [0.9, 0.1]),
+    (1, 2, 16, 256, 512, "f32", True, "inplace", [0.97, 1.0]),
+    (1, 130, 11, 4, 4, "f32", True, "new", None),
+    (2, 4, 1, 256, 512, "bf16", True, "inplace", [0.9, 0.95, 0.99, 0.999]),
+    (2, 2, 6, 64, 192, "bf16", True, "new", [0.0, 0.8]),
+    (1, 2, 16, 128, 256, "bf16", False, "new", [0.99, 0.5]),
+    (1, 2, 13, 100, 301, "bf16", True, "inplace", [0.7, 1.0]),
+]
+
+
+@pytest.mark.parametrize("B,H,T,dk,dv,dt,with_in,out,gs", SHORT_CASES)
+def test_short_block_vs_oracle(B, H, T, dk, dv, dt, with_in, out, gs):
+    """Blocks of at most 16 tokens take the one-pass streaming kernel (any C):
+    y and the carried state against the oracle, with state_in absent or given,
+    state_out absent, separate or the same buffer as state_in."""
+    say(f"short block B{B} H{H} T{T} dk{dk} dv{dv} {dt} state_in={with_in} state_out={out}")
+    gs = gs if gs is not None else gammas_for(H)
+    q, k, v, s0 = make_inputs(B, H, T, dk, dv, dt, seed=11, with_state=True)
+    if not with_in:
+        s0 = None
+    y_ref, s_ref = oracle.recurrent(q, k, v, torch.tensor(gs, dtype=torch.float32), s0)
+    qd, kd, vd, sd = to_dev(q, k, v, s0)
+    if out == "inplace":
+        so = sd
+    else:
+        so = out == "new"
+    y, s = ret.chunkwise_fwd(qd, kd, vd, gs, 64, state_in=sd, state_out=so)
+    torch.cuda.synchronize()
+    bound = tol(q.dtype)
+    check("y", y, y_ref, bound)
+    if out is not None:
+        check("state_out", s, s_ref, bound)
+    else:
+        assert s is None
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_parallel_vs_oracle(dt):
     B, H, T, dk, dv = 2, 3, 150, 32, 64
