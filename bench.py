@@ -11,7 +11,9 @@ reads cold data (one set, 201 MB, would fit in the 256 MB last-level cache).
 
 The recurrent decode step (retention_recurrent_step, batch 128, H=16, fp32
 256x512 state per head, 1000 chained steps) is measured in the same run and
-reported in the "decode" object.
+reported in the "decode" object, and a chunkwise continuation of 16 new tokens
+per stream from that state (the short-block streaming kernel) in the
+"continuation" object.
 
 Prints ONE JSON line.  "value" is whole-job throughput over the timed loop.
 The roofline of the chunkwise kernel uses algorithmic HBM bytes (bf16 Q, K, V
@@ -213,6 +215,31 @@ def main():
     del dq, dk_, dv_, state
     torch.cuda.empty_cache()
 
+    # ------------------------------------- multi-token continuation (16 tokens)
+    # chunkwise on 16 new tokens per stream from the decode state, in place
+    # (the short-block streaming kernel)
+    ct = 16
+    cq, ck, cv = make_inputs(dw.B, dw.H, ct, dw.dk, dw.dv, dw.dtype, seed=1)
+    cq, ck, cv = cq.to(dev), ck.to(dev), cv.to(dev)
+    cstate = s0.to(dev)
+    cy = torch.empty(dw.B, dw.H, ct, dw.dv, dtype=cq.dtype, device=dev)
+    for _ in range(3):
+        ret.chunkwise_fwd(cq, ck, cv, gd, ct, state_in=cstate, state_out=cstate, y=cy)
+    torch.cuda.synchronize()
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for a, b in cev:
+        a.record(stream)
+        ret.chunkwise_fwd(cq, ck, cv, gd, ct, state_in=cstate, state_out=cstate, y=cy)
+        b.record(stream)
+    torch.cuda.synchronize()
+    cont_us = statistics.median(a.elapsed_time(b) for a, b in cev) * 1e3
+    cont_bytes = 2 * state_bytes + dw.B * dw.H * ct * (2 * dw.dk + 2 * dw.dk + 2 * dw.dv + 2 * dw.dv)
+    cont_gbs = cont_bytes / (cont_us * 1e-6) / 1e9
+    cont_src = os.path.join(ROOT, "retnet_retention_chunkwise_amd", "csrc", "short_chunk.hip")
+    cont_traffic = load_traffic("short_chunk_continuation16_traffic.txt", cont_src)
+    del cq, ck, cv, cstate, cy, s0
+    torch.cuda.empty_cache()
+
     out = {
         "metric": "retention tokens/sec (chunkwise fwd) + decode steps/sec; % MFMA / HBM peak",
         "value": value,
@@ -253,6 +280,15 @@ def main():
                          "frac": dec_gbs / HBM_PEAK_GBS, "traffic": dec_traffic,
                          "algorithmic_bytes_per_launch": dec_bytes},
         },
+    }
+    out["continuation"] = {
+        "workload": f"chunkwise fwd on {ct} new tokens per stream from a carried state, in place: batch 128, H=16, "
+                    "fp32 state 256x512 per head, bf16 q/k/v",
+        "tokens_per_s": dw.B * ct / (cont_us * 1e-6),
+        "kernel_us": cont_us,
+        "roofline": {"bound": "hbm", "achieved": cont_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": cont_gbs / HBM_PEAK_GBS, "traffic": cont_traffic,
+                     "algorithmic_bytes_per_launch": cont_bytes},
     }
     if not args.no_cpu_baseline:
         sample_B = int(os.environ.get("RET_CPU_SAMPLE_B", str(wl.B)))
