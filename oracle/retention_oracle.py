@@ -34,19 +34,26 @@ Functions
   parallel(q, k, v, gamma, state_in)        -- brute-force parallel form
   chunkwise(q, k, v, gamma, C, state_in)    -- chunkwise form (derived, see below)
   chunk_state_contribution(...)             -- helper of the chunkwise form
+  recurrent_backward(q, k, v, gamma, dy, state_in, dstate_out)
+                                            -- gradients of the recurrent form
+                                               (chain rule; the pages give none)
 
 Tensors are torch tensors (any float dtype, any device is copied to the CPU)
 with layouts q, k: [B,H,T,d_k]; v: [B,H,T,d_v]; state: [B,H,d_k,d_v];
 gamma: [H].  Inputs are upcast exactly to float64 before any arithmetic.
 
 Parity status: every function above is pinned by tests/test_oracle.py against
-closed forms, a pure-Python brute force of the definition, and invariants.
+closed forms, a pure-Python brute force of the definition, and invariants;
+recurrent_backward against central finite differences of ``recurrent`` and
+the exact homogeneity identities of the operator (y is linear in q; y and the
+final state are linear in k, in v and in the initial state taken apart).
 """
 from __future__ import annotations
 
 import torch
 
-__all__ = ["recurrent", "recurrent_step", "parallel", "chunkwise", "chunk_state_contribution"]
+__all__ = ["recurrent", "recurrent_step", "parallel", "chunkwise", "chunk_state_contribution",
+           "recurrent_backward"]
 
 
 def _f64(x: torch.Tensor) -> torch.Tensor:
@@ -189,3 +196,46 @@ def chunkwise(q, k, v, gamma, C, state_in=None):
         # state carried to the next chunk
         R = torch.pow(g, float(L)).view(1, H, 1, 1) * R + chunk_state_contribution(kc, vc, g)
     return y, R
+
+
+def recurrent_backward(q, k, v, gamma, dy, state_in=None, dstate_out=None):
+    """Gradients of the recurrent form (the training use of the operator).
+
+    The aimpact page says the parallel form is the one parallelised for
+    training; it gives no backward pass, so this is the chain rule applied to
+    the recurrence of ``recurrent`` (S_n = gamma S_(n-1) + K_n^T V_n,
+    Y_n = Q_n S_n, S_(-1) = state_in, state_out = S_(T-1)) for the scalar
+    L = sum_n <dY_n, Y_n> + <dS_out, state_out>:
+
+        G_n      = dL/dS_n = Q_n^T dY_n + gamma G_(n+1)   (G_(T-1) also gets dS_out)
+        dQ_n     = dY_n S_n^T
+        dK_n     = G_n V_n^T,  i.e. dK_n[d] = sum_c G_n[d,c] V_n[c]
+        dV_n     = K_n G_n
+        dS_in    = gamma G_0                               (dS_out when T = 0)
+
+    dy: [B,H,T,dv]; dstate_out: [B,H,dk,dv] or None (zeros).  Returns
+    (dq [B,H,T,dk], dk [B,H,T,dk], dv [B,H,T,dv], dstate_in [B,H,dk,dv]), float64.
+    """
+    _check(q, k, v)
+    q, k, v, dy = _f64(q), _f64(k), _f64(v), _f64(dy)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if dy.shape != v.shape:
+        raise ValueError("dy must have the shape of v")
+    g = _gamma64(gamma, H).view(1, H, 1, 1)
+    # forward sweep: the states S_n, used at once for dQ_n
+    S = torch.zeros(B, H, dk, dv, dtype=torch.float64) if state_in is None else _f64(state_in).clone()
+    gq = torch.empty(B, H, T, dk, dtype=torch.float64)
+    for n in range(T):
+        S = g * S + k[:, :, n, :, None] * v[:, :, n, None, :]
+        gq[:, :, n, :] = torch.einsum("bhv,bhkv->bhk", dy[:, :, n, :], S)
+    # reverse sweep: carry = gradient reaching S_n from later steps (dS_out at n = T-1)
+    carry = torch.zeros(B, H, dk, dv, dtype=torch.float64) if dstate_out is None else _f64(dstate_out).clone()
+    gk = torch.empty(B, H, T, dk, dtype=torch.float64)
+    gv = torch.empty(B, H, T, dv, dtype=torch.float64)
+    for n in reversed(range(T)):
+        G = carry + q[:, :, n, :, None] * dy[:, :, n, None, :]       # G_n
+        gk[:, :, n, :] = torch.einsum("bhkv,bhv->bhk", G, v[:, :, n, :])
+        gv[:, :, n, :] = torch.einsum("bhk,bhkv->bhv", k[:, :, n, :], G)
+        carry = g * G                                                 # reaches S_(n-1)
+    return gq, gk, gv, carry

@@ -346,3 +346,137 @@ def test_pins_reject_planted_mistakes(kind):
 
 def test_pins_accept_the_oracle():
     assert not _pins_fail(oracle.recurrent)
+
+
+# ------------------------------------------------------------------ backward
+def _loss(q, k, v, gamma, s0, dy, ds):
+    """L = sum <dY, Y> + <dS_out, S_out> through the forward oracle."""
+    y, s = oracle.recurrent(q, k, v, gamma, s0)
+    return float((y * dy).sum() + (s * ds).sum())
+
+
+def _fd_grad(x, f, eps=1e-6):
+    """Central differences of the scalar f() with respect to every entry of x (in place)."""
+    g = torch.empty_like(x)
+    flat, gf = x.view(-1), g.view(-1)
+    for i in range(flat.numel()):
+        x0 = float(flat[i])
+        flat[i] = x0 + eps
+        up = f()
+        flat[i] = x0 - eps
+        dn = f()
+        flat[i] = x0
+        gf[i] = (up - dn) / (2 * eps)
+    return g
+
+
+def _backward_pins_fail(bwd):
+    """True if a pin rejects the backward candidate ``bwd`` (recurrent_backward's signature)."""
+    try:
+        # central finite differences of the forward oracle on tiny inputs,
+        # including gamma = 0 and gamma = 1 heads and a state on both ends
+        q, k, v, s0 = rand(1, 3, 5, 3, 4, seed=21, state=True)
+        gen = torch.Generator().manual_seed(22)
+        dy = torch.randn(v.shape, generator=gen, dtype=torch.float64)
+        ds = torch.randn(s0.shape, generator=gen, dtype=torch.float64)
+        gamma = torch.tensor([0.0, 0.7, 1.0])
+        gq, gk, gv, gs = bwd(q, k, v, gamma, dy, s0, ds)
+        f = lambda: _loss(q, k, v, gamma, s0, dy, ds)
+        for got, x in ((gq, q), (gk, k), (gv, v), (gs, s0)):
+            if rel(got, _fd_grad(x, f)) > 1e-8:
+                return True
+        # homogeneity identities on a larger case (exact up to rounding):
+        # Y is linear in Q; Y and S_out are linear in K, in V and in S_in taken apart
+        q, k, v, s0 = rand(2, 3, 40, 8, 6, seed=23, state=True)
+        dy = torch.randn(v.shape, generator=gen, dtype=torch.float64)
+        ds = torch.randn(s0.shape, generator=gen, dtype=torch.float64)
+        gamma = torch.tensor([0.5, 0.9, 0.999])
+        gq, gk, gv, gs = bwd(q, k, v, gamma, dy, s0, ds)
+        y, s = oracle.recurrent(q, k, v, gamma, s0)
+        y0, s_0 = oracle.recurrent(q, k, v, gamma)            # the part without S_in
+        full = float((y * dy).sum() + (s * ds).sum())
+        kv_part = float((y0 * dy).sum() + (s_0 * ds).sum())
+        checks = [
+            (float((gq * q).sum()), float((y * dy).sum())),
+            (float((gk * k).sum()), kv_part),
+            (float((gv * v).sum()), kv_part),
+            (float((gs * s0).sum()), full - kv_part),
+        ]
+        for a, b in checks:
+            if abs(a - b) > 1e-9 * max(1.0, abs(b)):
+                return True
+        # no dS_out and an empty sequence: dS_in = dS_out (zeros when absent)
+        z = bwd(q[:, :, :0], k[:, :, :0], v[:, :, :0], gamma, dy[:, :, :0], s0, ds)
+        if not torch.equal(z[3], ds):
+            return True
+    except Exception:
+        return True
+    return False
+
+
+def test_backward_pins_accept_the_oracle():
+    assert not _backward_pins_fail(oracle.recurrent_backward)
+
+
+def _backward_mutant(kind):
+    """recurrent_backward with one plausible slip each (planted here, on the CPU)."""
+
+    def run(q, k, v, gamma, dy, state_in=None, dstate_out=None):
+        B, H, T, dk = q.shape
+        dv = v.shape[-1]
+        g = torch.as_tensor(gamma, dtype=torch.float64).view(1, H, 1, 1)
+        S = torch.zeros(B, H, dk, dv, dtype=torch.float64) if state_in is None else state_in.clone()
+        gq = torch.empty(B, H, T, dk, dtype=torch.float64)
+        for n in range(T):
+            S_prev = S
+            S = g * S + k[:, :, n, :, None] * v[:, :, n, None, :]
+            use = S_prev if kind == "dq_previous_state" else S
+            gq[:, :, n] = torch.einsum("bhv,bhkv->bhk", dy[:, :, n], use)
+        carry = torch.zeros(B, H, dk, dv, dtype=torch.float64)
+        if dstate_out is not None and kind != "dstate_out_dropped":
+            carry = dstate_out.clone()
+        gk = torch.empty(B, H, T, dk, dtype=torch.float64)
+        gv = torch.empty(B, H, T, dv, dtype=torch.float64)
+        for n in reversed(range(T)):
+            G = carry + q[:, :, n, :, None] * dy[:, :, n, None, :]
+            if kind == "dk_uses_k":
+                gk[:, :, n] = torch.einsum("bhkv,bhv->bhk", G, dy[:, :, n])
+            else:
+                gk[:, :, n] = torch.einsum("bhkv,bhv->bhk", G, v[:, :, n])
+            gv[:, :, n] = torch.einsum("bhk,bhkv->bhv", k[:, :, n], G)
+            carry = G if kind == "no_decay_in_reverse" else g * G
+        if kind == "dstate_in_extra_decay":
+            carry = g * carry
+        return gq, gk, gv, carry
+
+    return run
+
+
+@pytest.mark.parametrize("kind", ["dq_previous_state", "dstate_out_dropped", "dk_uses_k", "no_decay_in_reverse",
+                                  "dstate_in_extra_decay"])
+def test_backward_pins_reject_planted_mistakes(kind):
+    assert _backward_pins_fail(_backward_mutant(kind)), kind
+
+
+def test_backward_chunk_form_matches_transposed_passes():
+    """The three chunkwise passes the GPU backward is built from, written with
+    the forward oracle on rearranged inputs, equal the chain-rule gradients:
+    dQ = forward retention of (dY, V, K) from S_in^T; dV and dK = forward
+    retention in reversed time of (K, Q, dY) and (V, dY, Q), whose cross term
+    carries one power of gamma less (the reversed initial state is dS_out
+    scaled by 1/gamma); dS_in = gamma * the final state of the dV pass."""
+    q, k, v, s0 = rand(2, 2, 23, 5, 7, seed=31, state=True)
+    gen = torch.Generator().manual_seed(32)
+    dy = torch.randn(v.shape, generator=gen, dtype=torch.float64)
+    ds = torch.randn(s0.shape, generator=gen, dtype=torch.float64)
+    gamma = torch.tensor([0.6, 0.95], dtype=torch.float64)
+    gq, gk, gv, gs = oracle.recurrent_backward(q, k, v, gamma, dy, s0, ds)
+    rev = lambda x: x.flip(2)
+    inv = (1.0 / gamma).view(1, 2, 1, 1)
+    dq, _ = oracle.recurrent(dy, v, k, gamma, s0.transpose(-1, -2))
+    dv_r, h = oracle.recurrent(rev(k), rev(q), rev(dy), gamma, inv * ds)
+    dk_r, _ = oracle.recurrent(rev(v), rev(dy), rev(q), gamma, inv * ds.transpose(-1, -2))
+    assert rel(dq, gq) < 1e-12
+    assert rel(rev(dv_r), gv) < 1e-12
+    assert rel(rev(dk_r), gk) < 1e-12
+    assert rel(gamma.view(1, 2, 1, 1) * h, gs) < 1e-12
