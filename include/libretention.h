@@ -105,6 +105,34 @@ ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, 
 size_t retention_chunkwise_workspace_bytes(int B, int H, int T, int dk, int dv, int C, ret_dtype dt);
 
 /*
+ * Backward of the chunkwise form: the gradients of retention_chunkwise_fwd for
+ * the loss L = sum <grad_y, y> + <grad_state_out, state_out>.  The aimpact page
+ * ("Il meccanismo") says the parallel form is the one run in parallel for
+ * training; the gradients are the chain rule applied to its recurrence
+ * S_n = gamma S_(n-1) + K_n^T V_n, Y_n = Q_n S_n, S_(-1) = state_in.  With
+ * G_n = dL/dS_n = Q_n^T dY_n + gamma G_(n+1) (G_(T-1) also receives
+ * grad_state_out):
+ *   grad_q[n] = dY_n S_n^T     grad_k[n] = G_n V_n^T     grad_v[n] = K_n G_n
+ *   grad_state_in = gamma G_0  (grad_state_out, or zeros, when T = 0)
+ * gamma (host) and the dtype dt are those of the forward call; q, k, v and
+ * state_in are the forward inputs (state_in nullable: zeros).
+ *   grad_y         : [B,H,T,dv] in dt.
+ *   grad_state_out : nullable (zeros); fp32 [B,H,dk,dv].
+ *   grad_q, grad_k : written, [B,H,T,dk] in dt.   grad_v : written, [B,H,T,dv] in dt.
+ *   grad_state_in  : nullable; written, fp32 [B,H,dk,dv].  May be the
+ *                    grad_state_out buffer exactly (in place).
+ * The written gradients must not overlap each other or any input (apart from
+ * that in-place case).  C is the chunk length of the forward call (validated
+ * like there); the gradients do not depend on it beyond rounding, and the
+ * kernels choose their own chunking.  Arithmetic is fp32 (bf16 inputs are
+ * widened; fp32 state and accumulators).
+ */
+ret_status retention_chunkwise_bwd(const void* q, const void* k, const void* v, const float* gamma,
+                                   const float* state_in, const void* grad_y, const float* grad_state_out,
+                                   void* grad_q, void* grad_k, void* grad_v, float* grad_state_in, int B, int H,
+                                   int T, int dk, int dv, int C, ret_dtype dt, void* stream);
+
+/*
  * One recurrent (decode) step, in place on the state: S <- gamma S + k^T v,
  * then y = q S (the new state, so the current token is included).  This is the
  * recurrent form of the aimpact page ("Il meccanismo"); the baulab page

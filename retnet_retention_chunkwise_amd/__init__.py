@@ -4,6 +4,8 @@ The compute lives in hand-written HIP kernels behind a C ABI
 (include/libretention.h); this package is the thin Python binding:
 
     chunkwise_fwd(q, k, v, gamma, C, state_in=None, state_out=True) -> (y, state_out)
+    chunkwise_bwd(q, k, v, gamma, C, grad_y, state_in=None, grad_state_out=None)
+        -> (grad_q, grad_k, grad_v, grad_state_in)
     parallel_fwd(q, k, v, gamma, state_in=None) -> y
     recurrent_step(q, k, v, gamma, state) -> y          (state updated in place)
 
@@ -15,6 +17,7 @@ from ._lib import (  # noqa: F401
     MAX_DK,
     MAX_DV,
     RetentionError,
+    chunkwise_bwd,
     chunkwise_fwd,
     chunkwise_workspace_bytes,
     last_error,

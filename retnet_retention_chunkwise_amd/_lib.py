@@ -28,6 +28,8 @@ SIGNATURES = {
     "retention_chunkwise_fwd": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "retention_chunkwise_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "retention_recurrent_step": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "retention_chunkwise_bwd": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                     _i, _vp]),
     "retention_last_error": (ctypes.c_char_p, []),
     "retention_version": (_i, []),
 }
@@ -176,6 +178,40 @@ def chunkwise_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma, C: i
                                      ws_bytes, _stream(q.device))
     _check(st)
     return y, state_out
+
+
+def chunkwise_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma, C: int, grad_y: torch.Tensor,
+                  state_in: Optional[torch.Tensor] = None, grad_state_out: Optional[torch.Tensor] = None,
+                  grad_state_in: Union[torch.Tensor, bool, None] = True
+                  ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    """Gradients of chunkwise_fwd on the GPU (retention_chunkwise_bwd).
+
+    q, k, v, gamma, C, state_in: the forward call's arguments.  grad_y: [B,H,T,dv]
+    in the input dtype; grad_state_out: optional fp32 [B,H,dk,dv].
+    grad_state_in: a tensor to fill (may be grad_state_out), True to allocate
+    one, or False/None for none.  Returns (grad_q, grad_k, grad_v, grad_state_in).
+    """
+    lib = load()
+    B, H, T, dk, dv, dt = _qkv(q, k, v)
+    _dev(grad_y, "grad_y")
+    if grad_y.shape != v.shape or grad_y.dtype != v.dtype or grad_y.device != v.device:
+        raise ValueError("grad_y must match v in shape, dtype and device")
+    sshape = (B, H, dk, dv)
+    _state_check(state_in, sshape, q.device, "state_in")
+    _state_check(grad_state_out, sshape, q.device, "grad_state_out")
+    if grad_state_in is True:
+        grad_state_in = torch.empty(sshape, dtype=torch.float32, device=q.device)
+    elif grad_state_in is False:
+        grad_state_in = None
+    _state_check(grad_state_in, sshape, q.device, "grad_state_in")
+    gq = torch.empty_like(q)
+    gk = torch.empty_like(k)
+    gv = torch.empty_like(v)
+    st = lib.retention_chunkwise_bwd(_ptr(q), _ptr(k), _ptr(v), _gamma_array(gamma, H), _ptr(state_in),
+                                     _ptr(grad_y), _ptr(grad_state_out), _ptr(gq), _ptr(gk), _ptr(gv),
+                                     _ptr(grad_state_in), B, H, T, dk, dv, int(C), dt, _stream(q.device))
+    _check(st)
+    return gq, gk, gv, grad_state_in
 
 
 def parallel_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma,

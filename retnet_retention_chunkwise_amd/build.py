@@ -29,6 +29,7 @@ SOURCES = [
     "chunkwise_mfma.hip",
     "state_copy.hip",
     "short_chunk.hip",
+    "chunkwise_bwd.hip",
 ]
 
 ARCH = "gfx950"

@@ -209,4 +209,53 @@ ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, 
   });
 }
 
+ret_status retention_chunkwise_bwd(const void* q, const void* k, const void* v, const float* gamma,
+                                   const float* state_in, const void* grad_y, const float* grad_state_out,
+                                   void* grad_q, void* grad_k, void* grad_v, float* grad_state_in, int B, int H,
+                                   int T, int dk, int dv, int C, ret_dtype dt, void* stream) {
+  const char* fn = "retention_chunkwise_bwd";
+  ret_status st = check_common(fn, B, H, T, dk, dv, dt, gamma);
+  if (st != RET_OK) return st;
+  if (C < 1) return fail(RET_ERR_INVALID_ARG, "%s: chunk length C=%d must be >= 1", fn, C);
+  if (C > RET_MAX_CHUNK) return fail(RET_ERR_UNSUPPORTED, "%s: chunk length C=%d exceeds %d", fn, C, RET_MAX_CHUNK);
+  if (T > 0 && (!q || !k || !v || !grad_y || !grad_q || !grad_k || !grad_v))
+    return fail(RET_ERR_INVALID_ARG, "%s: q, k, v, grad_y, grad_q, grad_k and grad_v are required", fn);
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(state_in) || misaligned(grad_y) ||
+      misaligned(grad_state_out) || misaligned(grad_q) || misaligned(grad_k) || misaligned(grad_v) ||
+      misaligned(grad_state_in))
+    return fail(RET_ERR_UNSUPPORTED, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (!ret::chunkwise_bwd_generic_supports(dk, dv))
+    return fail(RET_ERR_UNSUPPORTED, "%s: dk=%d, dv=%d not supported", fn, dk, dv);
+  const size_t es = dsize(dt);
+  const size_t bht = static_cast<size_t>(B) * H * T;
+  const size_t nk = bht * dk * es, nv = bht * dv * es;
+  const size_t ns = static_cast<size_t>(B) * H * dk * dv * 4;
+  struct Buf {
+    const void* p;
+    size_t n;
+  };
+  const Buf ins[] = {{q, nk}, {k, nk}, {v, nv}, {grad_y, nv}, {state_in, ns}, {grad_state_out, ns}};
+  const Buf outs[] = {{grad_q, nk}, {grad_k, nk}, {grad_v, nv}, {grad_state_in, ns}};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j) {
+      const bool in_place = i == 3 && j == 5 && outs[i].p == ins[j].p;
+      if (!in_place && overlap(outs[i].p, outs[i].n, ins[j].p, ins[j].n))
+        return fail(RET_ERR_INVALID_ARG, "%s: a gradient output overlaps an input", fn);
+    }
+    for (int j = 0; j < i; ++j)
+      if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+        return fail(RET_ERR_INVALID_ARG, "%s: gradient outputs overlap", fn);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    if (grad_state_in == nullptr || grad_state_in == grad_state_out) return ok();
+    const hipError_t e = ret::launch_state_copy(grad_state_out, grad_state_in, ns / 4, s);
+    return e == hipSuccess ? ok() : hip_fail(fn, e);
+  }
+  const ret::BwdArgs a{q, k, v, state_in, grad_y, grad_state_out, grad_q, grad_k, grad_v, grad_state_in};
+  return for_head_groups(fn, H, gamma, [&](const ret::HeadGroup& g) {
+    return ret::launch_chunkwise_bwd_generic(a, B, H, T, dk, dv, static_cast<int>(dt), g, s);
+  });
+}
+
 }  // extern "C"

@@ -57,6 +57,24 @@ hipError_t launch_short_chunk(const void* q, const void* k, const void* v, const
                               void* y, int B, int H, int T, int dk, int dv, int dt, const HeadGroup& g,
                               hipStream_t s);
 
+// Backward of the chunkwise form (gradients of retention_chunkwise_fwd).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* state_in;    // nullable
+  const void* dy;
+  const float* dstate_out;  // nullable
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dstate_in;         // nullable; may be dstate_out
+};
+// Generic fp32-arithmetic passes (any dtype, dk and dv up to 512).
+bool chunkwise_bwd_generic_supports(int dk, int dv);
+hipError_t launch_chunkwise_bwd_generic(const BwdArgs& a, int B, int H, int T, int dk, int dv, int dt,
+                                        const HeadGroup& g, hipStream_t s);
+
 // Copies state_in (or zeros when null) into state_out: the T = 0 case.
 hipError_t launch_state_copy(const float* state_in, float* state_out, size_t n, hipStream_t s);
 

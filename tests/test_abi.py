@@ -169,3 +169,38 @@ def test_host_dispatch_of_every_parity_shape_without_a_device(lib):
         st = lib.retention_chunkwise_fwd(q, k, v, gam(*([0.5] * H)), None, None, y, B, H, T, dk, dv, 64, d, None, 0,
                                          None)
         assert st == 3, (B, H, T, dk, dv, dt, _lib.last_error())
+
+
+def bwd(lib, q=FAKE, k=ctypes.c_void_p(0x100000), v=ctypes.c_void_p(0x200000), sin=None,
+        dy=ctypes.c_void_p(0x300000), dso=None, gq=ctypes.c_void_p(0x400000), gk=ctypes.c_void_p(0x500000),
+        gv=ctypes.c_void_p(0x600000), gsi=None, B=1, H=2, T=8, dk=16, dv=16, C=4, dt=0):
+    return lib.retention_chunkwise_bwd(q, k, v, gam(0.5, 0.9), sin, dy, dso, gq, gk, gv, gsi, B, H, T, dk, dv, C, dt,
+                                       None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(B=0), INVALID, "B=0"),
+    (dict(C=0), INVALID, "chunk length"),
+    (dict(C=129), UNSUPPORTED, "exceeds"),
+    (dict(dk=257), UNSUPPORTED, "exceed"),
+    (dict(dt=3), UNSUPPORTED, "dtype"),
+    (dict(dy=None), INVALID, "required"),
+    (dict(gk=None), INVALID, "required"),
+    (dict(gv=FAKE_MIS), UNSUPPORTED, "aligned"),
+    (dict(gq=FAKE), INVALID, "overlaps an input"),
+    (dict(gk=ctypes.c_void_p(0x400100)), INVALID, "outputs overlap"),
+    (dict(dso=ctypes.c_void_p(0x700000), gsi=ctypes.c_void_p(0x700010)), INVALID, "overlaps an input"),
+])
+def test_chunkwise_bwd_rejects(lib, kw, status, needle):
+    assert bwd(lib, **kw) == status
+    assert needle in _lib.last_error(), _lib.last_error()
+
+
+def test_chunkwise_bwd_in_place_state_gradient_passes_validation(lib):
+    """grad_state_in == grad_state_out is accepted; with no device the call then
+    fails only at the launch.  Skipped where a GPU is visible."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("placeholder pointers must never reach a real device")
+    st = bwd(lib, dso=ctypes.c_void_p(0x700000), gsi=ctypes.c_void_p(0x700000))
+    assert st == 3, _lib.last_error()

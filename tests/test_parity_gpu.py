@@ -152,6 +152,64 @@ def test_short_block_vs_oracle(B, H, T, dk, dv, dt, with_in, out, gs):
         assert s is None
 
 
+# ------------------------------------------------------------------ backward
+BWD_CASES = [
+    # B, H, T, dk, dv, C, dtype, state_in, grad_state_out, gammas
+    (1, 2, 37, 16, 24, 16, "f32", True, True, [0.9, 0.5]),
+    (2, 3, 100, 64, 64, 64, "f32", False, True, [0.0, 0.8, 1.0]),
+    (1, 2, 5, 7, 5, 4, "f32", True, False, [0.6, 0.99]),
+    (1, 1, 1, 8, 8, 1, "f32", True, True, [0.7]),
+    (1, 130, 20, 4, 4, 4, "f32", True, True, None),
+    (2, 2, 70, 256, 512, 64, "f32", True, True, [0.97, 0.999]),
+    (1, 2, 129, 128, 256, 64, "bf16", True, True, [0.99, 0.9]),
+    (1, 2, 200, 256, 512, 64, "bf16", True, True, [0.97, 0.999]),
+    (2, 2, 77, 48, 80, 32, "bf16", False, False, [0.0, 1.0]),
+]
+
+
+def bwd_inputs(B, H, T, dk, dv, dt, seed):
+    q, k, v, s0 = make_inputs(B, H, T, dk, dv, dt, seed=seed, with_state=True)
+    _, _, dy, ds = make_inputs(B, H, T, dk, dv, dt, seed=seed + 1000, with_state=True)
+    return q, k, v, s0, dy, ds
+
+
+@pytest.mark.parametrize("B,H,T,dk,dv,C,dt,with_in,with_dout,gs", BWD_CASES)
+def test_chunkwise_bwd_vs_oracle(B, H, T, dk, dv, C, dt, with_in, with_dout, gs):
+    """Gradients of the chunkwise forward (dQ, dK, dV, dS_in) against the
+    oracle's chain-rule gradients of the recurrent form."""
+    say(f"backward B{B} H{H} T{T} dk{dk} dv{dv} C{C} {dt} state_in={with_in} grad_state_out={with_dout}")
+    gs = gs if gs is not None else gammas_for(H)
+    q, k, v, s0, dy, ds = bwd_inputs(B, H, T, dk, dv, dt, seed=40)
+    s0 = s0 if with_in else None
+    ds = ds if with_dout else None
+    ref = oracle.recurrent_backward(q, k, v, torch.tensor(gs, dtype=torch.float32), dy, s0, ds)
+    qd, kd, vd, sd, dyd, dsd = to_dev(q, k, v, s0, dy, ds)
+    got = ret.chunkwise_bwd(qd, kd, vd, gs, C, dyd, state_in=sd, grad_state_out=dsd)
+    torch.cuda.synchronize()
+    bound = tol(q.dtype)
+    for name, g, r in zip(("grad_q", "grad_k", "grad_v", "grad_state_in"), got, ref):
+        check(name, g, r, bound)
+
+
+def test_chunkwise_bwd_in_place_state_gradient_and_empty_sequence():
+    """grad_state_in may be the grad_state_out buffer; T = 0 copies it through."""
+    B, H, T, dk, dv = 1, 2, 50, 32, 64
+    gs = [0.9, 0.6]
+    say("backward in place / T = 0")
+    q, k, v, s0, dy, ds = bwd_inputs(B, H, T, dk, dv, "f32", seed=41)
+    ref = oracle.recurrent_backward(q, k, v, torch.tensor(gs), dy, s0, ds)
+    qd, kd, vd, sd, dyd, dsd = to_dev(q, k, v, s0, dy, ds)
+    got = ret.chunkwise_bwd(qd, kd, vd, gs, 16, dyd, state_in=sd, grad_state_out=dsd, grad_state_in=dsd)
+    torch.cuda.synchronize()
+    for name, g, r in zip(("grad_q", "grad_k", "grad_v", "grad_state_in"), got, ref):
+        check(name, g, r, 1e-4)
+    e = lambda t: t[:, :, :0].contiguous()
+    ds2 = ds.to(DEV)
+    _, _, _, gsi = ret.chunkwise_bwd(e(qd), e(kd), e(vd), gs, 16, e(dyd), grad_state_out=ds2)
+    torch.cuda.synchronize()
+    assert torch.equal(gsi.cpu(), ds)
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_parallel_vs_oracle(dt):
     B, H, T, dk, dv = 2, 3, 150, 32, 64
