@@ -124,8 +124,9 @@ size_t retention_chunkwise_workspace_bytes(int B, int H, int T, int dk, int dv, 
  * The written gradients must not overlap each other or any input (apart from
  * that in-place case).  C is the chunk length of the forward call (validated
  * like there); the gradients do not depend on it beyond rounding, and the
- * kernels choose their own chunking.  Arithmetic is fp32 (bf16 inputs are
- * widened; fp32 state and accumulators).
+ * kernels choose their own chunking.  State and accumulators are fp32; bf16
+ * inputs with dk in {64, 128, 256} and dv in {64, 128, 256, 512} take bf16
+ * MFMA products (as the forward does), every other case fp32 arithmetic.
  */
 ret_status retention_chunkwise_bwd(const void* q, const void* k, const void* v, const float* gamma,
                                    const float* state_in, const void* grad_y, const float* grad_state_out,

@@ -30,6 +30,7 @@ SOURCES = [
     "state_copy.hip",
     "short_chunk.hip",
     "chunkwise_bwd.hip",
+    "chunkwise_bwd_mfma.hip",
 ]
 
 ARCH = "gfx950"

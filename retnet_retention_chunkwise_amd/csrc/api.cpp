@@ -253,7 +253,9 @@ ret_status retention_chunkwise_bwd(const void* q, const void* k, const void* v, 
     return e == hipSuccess ? ok() : hip_fail(fn, e);
   }
   const ret::BwdArgs a{q, k, v, state_in, grad_y, grad_state_out, grad_q, grad_k, grad_v, grad_state_in};
+  const bool mfma = ret::chunkwise_bwd_mfma_supports(dk, dv, static_cast<int>(dt));
   return for_head_groups(fn, H, gamma, [&](const ret::HeadGroup& g) {
+    if (mfma) return ret::launch_chunkwise_bwd_mfma(a, B, H, T, dk, dv, g, s);
     return ret::launch_chunkwise_bwd_generic(a, B, H, T, dk, dv, static_cast<int>(dt), g, s);
   });
 }

@@ -1,0 +1,292 @@
+// Backward passes of chunkwise retention on bf16 MFMA (gfx950), fp32 state.
+//
+// The gradients of the chunkwise form (aimpact page, "Il meccanismo:
+// Multi-Scale Retention"; chain rule on its recurrence) are three chunkwise
+// passes of one shape, each with a d_a x d_x fp32 state S:
+//   forward in time:  Out_j = gamma^(j+1) A_j S + sum_{j'<=j} gamma^(j-j') (A_j . B_j') X_j'
+//                     S <- gamma^L S + sum_j gamma^(L-1-j) B_j^T X_j
+//   reverse in time:  chunks from last to first,
+//                     Out_j = gamma^(L-1-j) A_j S + sum_{j'>=j} gamma^(j'-j) (A_j . B_j') X_j'
+//                     S <- gamma^L S + sum_j gamma^(j+1) B_j^T X_j
+//   dQ: forward, (A, B, X) = (dY, V, K), S_0 = S_in^T
+//   dK: reverse, (V, dY, Q), S_0 = dS_out^T
+//   dV: reverse, (K, Q, dY), S_0 = dS_out; the final S is dS_in.
+//
+// Work decomposition: a workgroup (4 waves) owns one (batch, head, tile of 64
+// X columns) and walks the 32-token chunks in order.  Wave w owns 16 columns
+// of the tile and keeps ALL d_a rows of their state in MFMA accumulator layout
+// (lane: column l%16, rows 4(l/16)+i of each 16-row block), so no state ever
+// goes through LDS:
+//   * the cross term is formed transposed, Out^T = S^T A^T: the accumulator
+//     layout of S, read as an MFMA A operand, covers the features
+//     {32s + 4g + i, 32s + 16 + 4g + i} of lane group g, and the matching B
+//     operand is two 8-byte reads of the A rows in LDS (the same feature
+//     permutation on both sides of the contraction);
+//   * the scores P = (A B^T) .* mask are one 16x16 tile per wave, written to
+//     LDS in bf16, and the intra term Out^T += X^T P^T reads X^T with the
+//     transposing LDS load;
+//   * the update S <- gamma^L S + B^T (z X) accumulates straight into the
+//     state registers, B^T and z X through the transposing load.
+// Out^T leaves each lane 4 consecutive columns of one token: 8-byte stores.
+// The next chunk's A, B and X are loaded into registers while the current
+// chunk is computed.  Global accesses go through buffer resources ending at
+// the sequence's last token, so rows past the end read as zero and their
+// stores are dropped.  dK and dQ (the same d_a) run in one launch.
+#include "common.h"
+#include "gfx950.h"
+#include "kernels.h"
+
+namespace ret {
+namespace {
+
+constexpr int kCT = 32;        // tokens per chunk
+constexpr int kTX = 64;        // X / Out columns per workgroup (16 per wave)
+constexpr int kThreads = 256;  // 4 waves
+
+struct MPass {
+  const uint16_t* a;  // [BH, T, DA] bf16
+  const uint16_t* b;  // [BH, T, DA]
+  const uint16_t* x;  // [BH, T, DX]
+  uint16_t* out;      // [BH, T, DX]
+  const float* s0;    // nullable; [BH, DA, DX] (s0_t = 0) or [BH, DX, DA] (s0_t = 1)
+  float* s_out;       // nullable; [BH, DA, DX]
+  int s0_t;
+  int rev;
+  int dx;
+};
+struct MPassSet {
+  MPass p[2];  // selected by blockIdx.z
+};
+
+template <int DA>
+struct BCfg {
+  static constexpr int ALD = DA + 8;    // bf16 row stride of the A and B tiles in LDS
+  static constexpr int XLD = kTX + 8;   // row stride of the X and zX tiles
+  static constexpr int PLD = kCT + 8;   // row stride of the score tile
+  static constexpr int NAB = DA / 16;   // 16-row state blocks per wave
+  static constexpr int NS = DA / 32;    // 32-wide k-steps over d_a
+  static constexpr int NLD = kCT * DA / 8 / kThreads;  // 16-byte loads of A (and of B) per thread
+  static_assert(NLD >= 1 && kCT * DA / 8 % kThreads == 0, "A/B tile split");
+};
+
+// d_a = 512 keeps 128 state registers per lane and takes the whole register
+// file (one workgroup per CU); smaller d_a leave room for two.
+template <int DA>
+__global__ __launch_bounds__(kThreads, DA >= 512 ? 1 : 2) void bwd_pass_mfma_kernel(MPassSet ps, HeadDecay gam,
+                                                                                     int H, int h0, int nh, int Tn) {
+  using F = BCfg<DA>;
+  __shared__ __attribute__((aligned(16))) uint16_t As[kCT * F::ALD];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[kCT * F::ALD];
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[kCT * F::XLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Zs[kCT * F::XLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[kCT * F::PLD];
+
+  const MPass p = ps.p[blockIdx.z];
+  const int DX = p.dx;
+  const bool rev = p.rev != 0;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int g = lane >> 4;   // lane group
+  const int lr = lane & 15;  // lane within the group
+  const int hl = blockIdx.y % nh;
+  const int bb = blockIdx.y / nh;
+  const long head = static_cast<long>(bb) * H + h0 + hl;
+  const float lg = gam.log2g[hl];
+  const int c0 = blockIdx.x * kTX;
+  const int cw = 16 * w;  // this wave's columns inside the tile
+
+  const rsrc_t ra = make_rsrc(p.a + head * Tn * DA, static_cast<uint32_t>(Tn) * DA * 2);
+  const rsrc_t rb = make_rsrc(p.b + head * Tn * DA, static_cast<uint32_t>(Tn) * DA * 2);
+  const rsrc_t rx = make_rsrc(p.x + head * Tn * DX, static_cast<uint32_t>(Tn) * DX * 2);
+  const rsrc_t ro = make_rsrc(p.out + head * Tn * DX, static_cast<uint32_t>(Tn) * DX * 2);
+  const long sb = head * static_cast<long>(DA) * DX;
+
+  // state: S[16 ab + 4 g + i][c0 + cw + lr] in Sacc[ab][i]
+  f32x4 Sacc[F::NAB];
+  {
+    const int x = c0 + cw + lr;
+#pragma unroll
+    for (int ab = 0; ab < F::NAB; ++ab) {
+      const int a = 16 * ab + 4 * g;
+      f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (p.s0 != nullptr) {
+        if (p.s0_t) {
+          v = *reinterpret_cast<const f32x4*>(p.s0 + sb + static_cast<long>(x) * DA + a);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = p.s0[sb + static_cast<long>(a + i) * DX + x];
+        }
+      }
+      Sacc[ab] = v;
+    }
+  }
+
+  // staging map: A/B piece r of this thread = row (tid + 256 r) / (DA/8), 8 features
+  constexpr int PPR = DA / 8;  // 16-byte pieces per row
+  u32x4 pa[F::NLD], pb[F::NLD], px;
+  const int xj = tid >> 3, xc = (tid & 7) * 8;  // X piece: row xj, columns xc..xc+7 of the tile
+  auto prefetch = [&](int t0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < F::NLD; ++r) {
+      const int q = tid + kThreads * r;
+      const uint32_t off = (static_cast<uint32_t>(t0 + q / PPR) * DA + (q % PPR) * 8) * 2;
+      pa[r] = buffer_load16(ra, off);
+      pb[r] = buffer_load16(rb, off);
+    }
+    px = buffer_load16(rx, (static_cast<uint32_t>(t0 + xj) * DX + c0 + xc) * 2);
+  };
+
+  const int nch = (Tn + kCT - 1) / kCT;
+  const float gL_full = gamma_pow(lg, kCT);
+  prefetch((rev ? nch - 1 : 0) * kCT);
+  for (int it = 0; it < nch; ++it) {
+    const int ci = rev ? nch - 1 - it : it;
+    const int t0 = ci * kCT;
+    const int L = min(kCT, Tn - t0);
+    // ---- stage this chunk (the previous chunk ended with a barrier)
+#pragma unroll
+    for (int r = 0; r < F::NLD; ++r) {
+      const int q = tid + kThreads * r;
+      const int o = (q / PPR) * F::ALD + (q % PPR) * 8;
+      *reinterpret_cast<u32x4*>(&As[o]) = pa[r];
+      *reinterpret_cast<u32x4*>(&Bs[o]) = pb[r];
+    }
+    {
+      *reinterpret_cast<u32x4*>(&Xs[xj * F::XLD + xc]) = px;
+      const float z = xj < L ? gamma_pow(lg, rev ? xj + 1 : L - 1 - xj) : 0.0f;
+      const bf16x8 xv = __builtin_bit_cast(bf16x8, px);
+      bf16x8 zv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zv[e] = static_cast<__bf16>(z * static_cast<float>(xv[e]));
+      *reinterpret_cast<bf16x8*>(&Zs[xj * F::XLD + xc]) = zv;
+    }
+    if (it + 1 < nch) prefetch((rev ? ci - 1 : ci + 1) * kCT);
+    lds_barrier();
+
+    // ---- scores: tile (jb, jpb) of wave w, masked and decayed, to LDS in bf16
+    {
+      const int jb = w >> 1, jpb = w & 1;
+      const bool live = rev ? jpb >= jb : jpb <= jb;
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (live) {
+#pragma unroll
+        for (int s = 0; s < F::NS; ++s) {
+          const bf16x8 av = lds_read16(&As[(16 * jb + lr) * F::ALD + 32 * s + 8 * g]);
+          const bf16x8 bv = lds_read16(&Bs[(16 * jpb + lr) * F::ALD + 32 * s + 8 * g]);
+          acc = mfma(av, bv, acc);
+        }
+      }
+      const int jp = 16 * jpb + lr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 16 * jb + 4 * g + i;
+        const int d = rev ? jp - j : j - jp;
+        const float val = d >= 0 ? acc[i] * gamma_pow(lg, d) : 0.0f;
+        Ps[j * F::PLD + jp] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(val));
+      }
+    }
+    lds_barrier();
+
+    // ---- outputs: Out^T = diag-scaled S^T A^T + X^T P^T, two 16-token blocks
+    f32x4 O[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) O[jb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < F::NS; ++s) {
+      const bf16x8 sv = pack_bf16x8(Sacc[2 * s], Sacc[2 * s + 1]);
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const uint16_t* row = &As[(16 * jb + lr) * F::ALD + 32 * s + 4 * g];
+        const bf16x8 av = join(*reinterpret_cast<const s16x4*>(row), *reinterpret_cast<const s16x4*>(row + 16));
+        O[jb] = mfma(sv, av, O[jb]);
+      }
+    }
+    {
+      const uint16_t* xr = &Xs[(8 * g + (lr >> 2)) * F::XLD + cw + 4 * (lr & 3)];
+      const bf16x8 xt = join(lds_read_tr(xr), lds_read_tr(xr + 4 * F::XLD));
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const int j = 16 * jb + lr;
+        const float wj = j < L ? gamma_pow(lg, rev ? L - 1 - j : j + 1) : 0.0f;
+        O[jb] *= wj;
+        const bf16x8 pv = lds_read16(&Ps[j * F::PLD + 8 * g]);
+        O[jb] = mfma(xt, pv, O[jb]);
+        u32x2 st;
+        st[0] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(O[jb][0]))) |
+                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(O[jb][1]))) << 16);
+        st[1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(O[jb][2]))) |
+                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(O[jb][3]))) << 16);
+        buffer_store8(ro, (static_cast<uint32_t>(t0 + j) * DX + c0 + cw + 4 * g) * 2, st);
+      }
+    }
+
+    // ---- state update: S <- gamma^L S + B^T (z X)
+    {
+      const float gL = L == kCT ? gL_full : gamma_pow(lg, L);
+      const uint16_t* zr = &Zs[(8 * g + (lr >> 2)) * F::XLD + cw + 4 * (lr & 3)];
+      const bf16x8 zx = join(lds_read_tr(zr), lds_read_tr(zr + 4 * F::XLD));
+      const uint16_t* br = &Bs[(8 * g + (lr >> 2)) * F::ALD + 4 * (lr & 3)];
+#pragma unroll
+      for (int ab = 0; ab < F::NAB; ++ab) {
+        const bf16x8 bt = join(lds_read_tr(br + 16 * ab), lds_read_tr(br + 16 * ab + 4 * F::ALD));
+        Sacc[ab] = mfma(bt, zx, Sacc[ab] * gL);
+      }
+    }
+    lds_barrier();  // every read of this chunk's tiles is done
+  }
+
+  if (p.s_out != nullptr) {
+    const int x = c0 + cw + lr;
+#pragma unroll
+    for (int ab = 0; ab < F::NAB; ++ab)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p.s_out[sb + static_cast<long>(16 * ab + 4 * g + i) * DX + x] = Sacc[ab][i];
+  }
+}
+
+template <int DA>
+void launch_da(const MPassSet& ps, int nz, int dx, int B, const HeadDecay& hd, int H, const HeadGroup& g, int T,
+               hipStream_t s) {
+  const dim3 grid(dx / kTX, B * g.nh, nz);
+  hipLaunchKernelGGL(bwd_pass_mfma_kernel<DA>, grid, dim3(kThreads), 0, s, ps, hd, H, g.h0, g.nh, T);
+}
+
+void launch_by_da(int da, const MPassSet& ps, int nz, int dx, int B, const HeadDecay& hd, int H, const HeadGroup& g,
+                  int T, hipStream_t s) {
+  switch (da) {
+    case 64: launch_da<64>(ps, nz, dx, B, hd, H, g, T, s); break;
+    case 128: launch_da<128>(ps, nz, dx, B, hd, H, g, T, s); break;
+    case 256: launch_da<256>(ps, nz, dx, B, hd, H, g, T, s); break;
+    default: launch_da<512>(ps, nz, dx, B, hd, H, g, T, s); break;
+  }
+}
+
+bool da_ok(int d) { return d == 64 || d == 128 || d == 256 || d == 512; }
+
+}  // namespace
+
+bool chunkwise_bwd_mfma_supports(int dk, int dv, int dt) { return dt == 1 && da_ok(dk) && da_ok(dv); }
+
+hipError_t launch_chunkwise_bwd_mfma(const BwdArgs& a, int B, int H, int T, int dk, int dv, const HeadGroup& g,
+                                     hipStream_t s) {
+  const HeadDecay hd = make_head_decay(g);
+  auto u = [](const void* x) { return static_cast<const uint16_t*>(x); };
+  // dK (reverse over V, dY, Q from dS_out^T) and dQ (forward over dY, V, K from
+  // S_in^T) share d_a = dv: one launch, blockIdx.z selects the pass
+  MPassSet kq{};
+  kq.p[0] = MPass{u(a.v), u(a.dy), u(a.q), static_cast<uint16_t*>(a.dk), a.dstate_out, nullptr, 1, 1, dk};
+  kq.p[1] = MPass{u(a.dy), u(a.v), u(a.k), static_cast<uint16_t*>(a.dq), a.state_in, nullptr, 1, 0, dk};
+  launch_by_da(dv, kq, 2, dk, B, hd, H, g, T, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // dV (reverse over K, Q, dY from dS_out); final state = dS_in.  After the dK
+  // pass, so that dstate_in may be the dstate_out buffer.
+  MPassSet vs{};
+  vs.p[0] = MPass{u(a.k), u(a.q), u(a.dy), static_cast<uint16_t*>(a.dv), a.dstate_out, a.dstate_in, 0, 1, dv};
+  vs.p[1] = vs.p[0];
+  launch_by_da(dk, vs, 1, dv, B, hd, H, g, T, s);
+  return hipGetLastError();
+}
+
+}  // namespace ret

@@ -41,64 +41,13 @@
 #include <type_traits>
 
 #include "common.h"
+#include "gfx950.h"
 #include "kernels.h"
 
 namespace ret {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
 constexpr int kTN = 64;  // value columns per workgroup
-
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// Transposing LDS read: within each 16-lane group, lane j receives element
-// (j % 4) of the 4-element row read by lane 4*e + j/4, for e = 0..3.
-__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-}
-
-__device__ __forceinline__ bf16x8 join(s16x4 lo, s16x4 hi) {
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-__device__ __forceinline__ bf16x8 lds_read16(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
-
-// Workgroup barrier for hand-offs through LDS.  The fences cover LDS only, so
-// a wave waits for its own LDS accesses but not for its global loads and
-// stores in flight: the K/V/Q loads of later chunks and the Y stores stay
-// outstanding across the barrier (a __syncthreads() fence would drain them).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// Raw buffer resource over [base, base + bytes): loads past the end return 0,
-// stores past the end are dropped.  0x00020000 is the gfx9 data-format word.
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
-                                           0x00020000);
-}
-__device__ __forceinline__ u32x4 buffer_load16(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
-}
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void buffer_store8(rsrc_t r, uint32_t off, u32x2 x) {
-  __builtin_amdgcn_raw_buffer_store_b64(x, r, static_cast<int>(off), 0, 0);
-}
 
 template <int CT, int DK>
 struct Cfg {

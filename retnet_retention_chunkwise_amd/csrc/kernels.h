@@ -74,6 +74,10 @@ struct BwdArgs {
 bool chunkwise_bwd_generic_supports(int dk, int dv);
 hipError_t launch_chunkwise_bwd_generic(const BwdArgs& a, int B, int H, int T, int dk, int dv, int dt,
                                         const HeadGroup& g, hipStream_t s);
+// bf16 MFMA passes: bf16 inputs with dk, dv in {64, 128, 256, 512}.
+bool chunkwise_bwd_mfma_supports(int dk, int dv, int dt);
+hipError_t launch_chunkwise_bwd_mfma(const BwdArgs& a, int B, int H, int T, int dk, int dv, const HeadGroup& g,
+                                     hipStream_t s);
 
 // Copies state_in (or zeros when null) into state_out: the T = 0 case.
 hipError_t launch_state_copy(const float* state_in, float* state_out, size_t n, hipStream_t s);

@@ -204,3 +204,18 @@ def test_chunkwise_bwd_in_place_state_gradient_passes_validation(lib):
         pytest.skip("placeholder pointers must never reach a real device")
     st = bwd(lib, dso=ctypes.c_void_p(0x700000), gsi=ctypes.c_void_p(0x700000))
     assert st == 3, _lib.last_error()
+
+
+def test_host_dispatch_of_every_backward_parity_shape_without_a_device(lib):
+    """Every backward parity shape passes validation on the host and fails only
+    at the launch when no GPU is present.  Skipped where a GPU is visible."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("placeholder pointers must never reach a real device")
+    import test_parity_gpu as parity
+    for (B, H, T, dk, dv, C, dt, _, _, _) in parity.BWD_CASES:
+        d = 1 if dt == "bf16" else 0
+        ptrs = [ctypes.c_void_p(a << 36) for a in range(1, 8)]
+        st = lib.retention_chunkwise_bwd(ptrs[0], ptrs[1], ptrs[2], gam(*([0.5] * H)), None, ptrs[3], None,
+                                         ptrs[4], ptrs[5], ptrs[6], None, B, H, T, dk, dv, C, d, None)
+        assert st == 3, (B, H, T, dk, dv, C, dt, _lib.last_error())

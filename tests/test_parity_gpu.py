@@ -164,6 +164,13 @@ BWD_CASES = [
     (1, 2, 129, 128, 256, 64, "bf16", True, True, [0.99, 0.9]),
     (1, 2, 200, 256, 512, 64, "bf16", True, True, [0.97, 0.999]),
     (2, 2, 77, 48, 80, 32, "bf16", False, False, [0.0, 1.0]),
+    # bf16 MFMA passes: every d_a instance (64..512), ragged last chunks, gamma 0 and 1
+    (2, 2, 100, 64, 64, 16, "bf16", True, True, [0.0, 1.0]),
+    (1, 3, 65, 128, 128, 64, "bf16", False, True, [0.5, 0.9, 0.999]),
+    (1, 2, 31, 64, 512, 32, "bf16", True, False, [0.95, 0.7]),
+    (2, 2, 257, 256, 512, 128, "bf16", False, False, [0.999, 0.8]),
+    (1, 2, 1, 256, 256, 1, "bf16", True, True, [0.9, 0.6]),
+    (1, 130, 40, 64, 64, 32, "bf16", True, True, None),
 ]
 
 
@@ -189,6 +196,25 @@ def test_chunkwise_bwd_vs_oracle(B, H, T, dk, dv, C, dt, with_in, with_dout, gs)
     bound = tol(q.dtype)
     for name, g, r in zip(("grad_q", "grad_k", "grad_v", "grad_state_in"), got, ref):
         check(name, g, r, bound)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_chunkwise_bwd_sampled_heads_at_layer_size(dt):
+    """The backward at the 1.3B-scale layer shape (B4 H8 T2048 dk256 dv512):
+    two sampled heads against the oracle (their gradients depend only on their
+    own inputs)."""
+    wl = WORKLOADS["layer1p3b"]
+    say(f"backward at layer size, {dt}")
+    q, k, v, s0, dy, ds = bwd_inputs(wl.B, wl.H, wl.T, wl.dk, wl.dv, dt, seed=42)
+    gs = list(wl.gammas)
+    qd, kd, vd, sd, dyd, dsd = to_dev(q, k, v, s0, dy, ds)
+    got = ret.chunkwise_bwd(qd, kd, vd, gs, wl.C, dyd, state_in=sd, grad_state_out=dsd)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (3, 7)):
+        sl = lambda t: t[b:b + 1, h:h + 1]
+        ref = oracle.recurrent_backward(sl(q), sl(k), sl(v), torch.tensor([gs[h]]), sl(dy), sl(s0), sl(ds))
+        for name, gg, r in zip(("grad_q", "grad_k", "grad_v", "grad_state_in"), got, ref):
+            check(f"{name} (b{b} h{h})", sl(gg), r, tol(q.dtype))
 
 
 def test_chunkwise_bwd_in_place_state_gradient_and_empty_sequence():
