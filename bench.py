@@ -240,6 +240,28 @@ def main():
     del cq, ck, cv, cstate, cy, s0
     torch.cuda.empty_cache()
 
+    # ------------------------------------------------ backward (layer1p3b)
+    # gradients of the chunkwise forward: dQ, dK, dV and dS_in from dY and dS_out
+    bq, bk, bv, bs0 = make_inputs(wl.B, wl.H, wl.T, wl.dk, wl.dv, wl.dtype, seed=7, with_state=True)
+    _, _, bdy, bds = make_inputs(wl.B, wl.H, wl.T, wl.dk, wl.dv, wl.dtype, seed=8, with_state=True)
+    bq, bk, bv, bs0, bdy, bds = (t.to(dev) for t in (bq, bk, bv, bs0, bdy, bds))
+    for _ in range(3):
+        ret.chunkwise_bwd(bq, bk, bv, g, wl.C, bdy, state_in=bs0, grad_state_out=bds)
+    torch.cuda.synchronize()
+    bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for a, b in bev:
+        a.record(stream)
+        ret.chunkwise_bwd(bq, bk, bv, g, wl.C, bdy, state_in=bs0, grad_state_out=bds)
+        b.record(stream)
+    torch.cuda.synchronize()
+    bwd_us = statistics.median(a.elapsed_time(b) for a, b in bev) * 1e3
+    bwd_bytes = head_tokens * (2 * wl.dk * 2 + 2 * wl.dv * 2 + 2 * wl.dk * 2 + wl.dv * 2)  # q,k,v,dy in; dq,dk,dv out
+    bwd_flops = 3 * alg_flops  # three chunkwise passes of the forward's per-token work
+    bwd_src = os.path.join(ROOT, "retnet_retention_chunkwise_amd", "csrc", "chunkwise_bwd_mfma.hip")
+    bwd_traffic = load_traffic("chunkwise_bwd_mfma_layer1p3b_traffic.txt", bwd_src)
+    del bq, bk, bv, bs0, bdy, bds
+    torch.cuda.empty_cache()
+
     out = {
         "metric": "retention tokens/sec (chunkwise fwd) + decode steps/sec; % MFMA / HBM peak",
         "value": value,
@@ -289,6 +311,18 @@ def main():
         "roofline": {"bound": "hbm", "achieved": cont_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": cont_gbs / HBM_PEAK_GBS, "traffic": cont_traffic,
                      "algorithmic_bytes_per_launch": cont_bytes},
+    }
+    out["backward"] = {
+        "workload": "chunkwise backward (dQ, dK, dV, dS_in) of the layer1p3b workload: B=4 H=8 T=2048 dk=256 "
+                    "dv=512 bf16 C=64, with state_in and grad_state_out",
+        "tokens_per_s": tokens / (bwd_us * 1e-6),
+        "kernel_us": bwd_us,
+        "roofline": {"bound": "hbm", "achieved": bwd_bytes / (bwd_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": bwd_bytes / (bwd_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": bwd_traffic, "algorithmic_bytes_per_launch": bwd_bytes,
+                     "algorithmic_flops_per_launch": bwd_flops,
+                     "mfma_tflops": bwd_flops / (bwd_us * 1e-6) / 1e12,
+                     "mfma_frac": bwd_flops / (bwd_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS},
     }
     if not args.no_cpu_baseline:
         sample_B = int(os.environ.get("RET_CPU_SAMPLE_B", str(wl.B)))

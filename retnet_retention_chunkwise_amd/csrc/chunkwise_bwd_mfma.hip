@@ -28,10 +28,15 @@
 //   * the update S <- gamma^L S + B^T (z X) accumulates straight into the
 //     state registers, B^T and z X through the transposing load.
 // Out^T leaves each lane 4 consecutive columns of one token: 8-byte stores.
+// In the operands read with the transposing load (X^T, B^T, z X), k index
+// 8g + e of lane group g stands for token 4g + (e % 4) + 16 (e / 4) (P^T is
+// read with the same order); with the B and X row strides padded to 8 dwords
+// mod 64 banks this makes those reads free of bank conflicts.
 // The next chunk's A, B and X are loaded into registers while the current
 // chunk is computed.  Global accesses go through buffer resources ending at
 // the sequence's last token, so rows past the end read as zero and their
-// stores are dropped.  dK and dQ (the same d_a) run in one launch.
+// stores are dropped.  dK and dQ (the same d_a) run in one launch; the column
+// tiles and passes of a head are placed on one XCD (shared L2).
 #include "common.h"
 #include "gfx950.h"
 #include "kernels.h"
@@ -55,13 +60,15 @@ struct MPass {
   int dx;
 };
 struct MPassSet {
-  MPass p[2];  // selected by blockIdx.z
+  MPass p[2];
+  int npass;  // passes of the launch (same d_a and d_x)
 };
 
 template <int DA>
 struct BCfg {
-  static constexpr int ALD = DA + 8;    // bf16 row stride of the A and B tiles in LDS
-  static constexpr int XLD = kTX + 8;   // row stride of the X and zX tiles
+  static constexpr int ALD = DA + 8;    // bf16 row stride of the A tile in LDS
+  static constexpr int BLD = DA + 16;   // row stride of the B tile
+  static constexpr int XLD = kTX + 16;  // row stride of the X and zX tiles
   static constexpr int PLD = kCT + 8;   // row stride of the score tile
   static constexpr int NAB = DA / 16;   // 16-row state blocks per wave
   static constexpr int NS = DA / 32;    // 32-wide k-steps over d_a
@@ -76,12 +83,22 @@ __global__ __launch_bounds__(kThreads, DA >= 512 ? 1 : 2) void bwd_pass_mfma_ker
                                                                                      int H, int h0, int nh, int Tn) {
   using F = BCfg<DA>;
   __shared__ __attribute__((aligned(16))) uint16_t As[kCT * F::ALD];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kCT * F::ALD];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[kCT * F::BLD];
   __shared__ __attribute__((aligned(16))) uint16_t Xs[kCT * F::XLD];
   __shared__ __attribute__((aligned(16))) uint16_t Zs[kCT * F::XLD];
   __shared__ __attribute__((aligned(16))) uint16_t Ps[kCT * F::PLD];
 
-  const MPass p = ps.p[blockIdx.z];
+  // Work item.  Workgroup ids are dealt round-robin over the 8 XCDs; the
+  // remap gives each XCD a contiguous range of items, so the column tiles and
+  // passes of one head (which read the same rows) share one L2.
+  const int nwg = gridDim.x;
+  const int lin = blockIdx.x;
+  const int item = (nwg % 8 == 0) ? (lin % 8) * (nwg / 8) + lin / 8 : lin;
+  const int tiles = ps.p[0].dx / kTX;
+  const int tile = item % tiles;
+  const int pz = (item / tiles) % ps.npass;
+  const int hitem = item / (tiles * ps.npass);
+  const MPass p = ps.p[pz];
   const int DX = p.dx;
   const bool rev = p.rev != 0;
   const int tid = threadIdx.x;
@@ -89,11 +106,11 @@ __global__ __launch_bounds__(kThreads, DA >= 512 ? 1 : 2) void bwd_pass_mfma_ker
   const int w = tid >> 6;
   const int g = lane >> 4;   // lane group
   const int lr = lane & 15;  // lane within the group
-  const int hl = blockIdx.y % nh;
-  const int bb = blockIdx.y / nh;
+  const int hl = hitem % nh;
+  const int bb = hitem / nh;
   const long head = static_cast<long>(bb) * H + h0 + hl;
   const float lg = gam.log2g[hl];
-  const int c0 = blockIdx.x * kTX;
+  const int c0 = tile * kTX;
   const int cw = 16 * w;  // this wave's columns inside the tile
 
   const rsrc_t ra = make_rsrc(p.a + head * Tn * DA, static_cast<uint32_t>(Tn) * DA * 2);
@@ -148,9 +165,8 @@ __global__ __launch_bounds__(kThreads, DA >= 512 ? 1 : 2) void bwd_pass_mfma_ker
 #pragma unroll
     for (int r = 0; r < F::NLD; ++r) {
       const int q = tid + kThreads * r;
-      const int o = (q / PPR) * F::ALD + (q % PPR) * 8;
-      *reinterpret_cast<u32x4*>(&As[o]) = pa[r];
-      *reinterpret_cast<u32x4*>(&Bs[o]) = pb[r];
+      *reinterpret_cast<u32x4*>(&As[(q / PPR) * F::ALD + (q % PPR) * 8]) = pa[r];
+      *reinterpret_cast<u32x4*>(&Bs[(q / PPR) * F::BLD + (q % PPR) * 8]) = pb[r];
     }
     {
       *reinterpret_cast<u32x4*>(&Xs[xj * F::XLD + xc]) = px;
@@ -173,7 +189,7 @@ __global__ __launch_bounds__(kThreads, DA >= 512 ? 1 : 2) void bwd_pass_mfma_ker
 #pragma unroll
         for (int s = 0; s < F::NS; ++s) {
           const bf16x8 av = lds_read16(&As[(16 * jb + lr) * F::ALD + 32 * s + 8 * g]);
-          const bf16x8 bv = lds_read16(&Bs[(16 * jpb + lr) * F::ALD + 32 * s + 8 * g]);
+          const bf16x8 bv = lds_read16(&Bs[(16 * jpb + lr) * F::BLD + 32 * s + 8 * g]);
           acc = mfma(av, bv, acc);
         }
       }
@@ -203,14 +219,15 @@ __global__ __launch_bounds__(kThreads, DA >= 512 ? 1 : 2) void bwd_pass_mfma_ker
       }
     }
     {
-      const uint16_t* xr = &Xs[(8 * g + (lr >> 2)) * F::XLD + cw + 4 * (lr & 3)];
-      const bf16x8 xt = join(lds_read_tr(xr), lds_read_tr(xr + 4 * F::XLD));
+      const uint16_t* xr = &Xs[(4 * g + (lr >> 2)) * F::XLD + cw + 4 * (lr & 3)];
+      const bf16x8 xt = join(lds_read_tr(xr), lds_read_tr(xr + 16 * F::XLD));
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
         const int j = 16 * jb + lr;
         const float wj = j < L ? gamma_pow(lg, rev ? L - 1 - j : j + 1) : 0.0f;
         O[jb] *= wj;
-        const bf16x8 pv = lds_read16(&Ps[j * F::PLD + 8 * g]);
+        const bf16x8 pv = join(*reinterpret_cast<const s16x4*>(&Ps[j * F::PLD + 4 * g]),
+                               *reinterpret_cast<const s16x4*>(&Ps[j * F::PLD + 16 + 4 * g]));
         O[jb] = mfma(xt, pv, O[jb]);
         u32x2 st;
         st[0] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(O[jb][0]))) |
@@ -224,12 +241,12 @@ __global__ __launch_bounds__(kThreads, DA >= 512 ? 1 : 2) void bwd_pass_mfma_ker
     // ---- state update: S <- gamma^L S + B^T (z X)
     {
       const float gL = L == kCT ? gL_full : gamma_pow(lg, L);
-      const uint16_t* zr = &Zs[(8 * g + (lr >> 2)) * F::XLD + cw + 4 * (lr & 3)];
-      const bf16x8 zx = join(lds_read_tr(zr), lds_read_tr(zr + 4 * F::XLD));
-      const uint16_t* br = &Bs[(8 * g + (lr >> 2)) * F::ALD + 4 * (lr & 3)];
+      const uint16_t* zr = &Zs[(4 * g + (lr >> 2)) * F::XLD + cw + 4 * (lr & 3)];
+      const bf16x8 zx = join(lds_read_tr(zr), lds_read_tr(zr + 16 * F::XLD));
+      const uint16_t* br = &Bs[(4 * g + (lr >> 2)) * F::BLD + 4 * (lr & 3)];
 #pragma unroll
       for (int ab = 0; ab < F::NAB; ++ab) {
-        const bf16x8 bt = join(lds_read_tr(br + 16 * ab), lds_read_tr(br + 16 * ab + 4 * F::ALD));
+        const bf16x8 bt = join(lds_read_tr(br + 16 * ab), lds_read_tr(br + 16 * ab + 16 * F::BLD));
         Sacc[ab] = mfma(bt, zx, Sacc[ab] * gL);
       }
     }
@@ -246,19 +263,19 @@ __global__ __launch_bounds__(kThreads, DA >= 512 ? 1 : 2) void bwd_pass_mfma_ker
 }
 
 template <int DA>
-void launch_da(const MPassSet& ps, int nz, int dx, int B, const HeadDecay& hd, int H, const HeadGroup& g, int T,
+void launch_da(const MPassSet& ps, int dx, int B, const HeadDecay& hd, int H, const HeadGroup& g, int T,
                hipStream_t s) {
-  const dim3 grid(dx / kTX, B * g.nh, nz);
+  const dim3 grid(dx / kTX * B * g.nh * ps.npass);
   hipLaunchKernelGGL(bwd_pass_mfma_kernel<DA>, grid, dim3(kThreads), 0, s, ps, hd, H, g.h0, g.nh, T);
 }
 
-void launch_by_da(int da, const MPassSet& ps, int nz, int dx, int B, const HeadDecay& hd, int H, const HeadGroup& g,
-                  int T, hipStream_t s) {
+void launch_by_da(int da, const MPassSet& ps, int dx, int B, const HeadDecay& hd, int H, const HeadGroup& g, int T,
+                  hipStream_t s) {
   switch (da) {
-    case 64: launch_da<64>(ps, nz, dx, B, hd, H, g, T, s); break;
-    case 128: launch_da<128>(ps, nz, dx, B, hd, H, g, T, s); break;
-    case 256: launch_da<256>(ps, nz, dx, B, hd, H, g, T, s); break;
-    default: launch_da<512>(ps, nz, dx, B, hd, H, g, T, s); break;
+    case 64: launch_da<64>(ps, dx, B, hd, H, g, T, s); break;
+    case 128: launch_da<128>(ps, dx, B, hd, H, g, T, s); break;
+    case 256: launch_da<256>(ps, dx, B, hd, H, g, T, s); break;
+    default: launch_da<512>(ps, dx, B, hd, H, g, T, s); break;
   }
 }
 
@@ -273,11 +290,12 @@ hipError_t launch_chunkwise_bwd_mfma(const BwdArgs& a, int B, int H, int T, int 
   const HeadDecay hd = make_head_decay(g);
   auto u = [](const void* x) { return static_cast<const uint16_t*>(x); };
   // dK (reverse over V, dY, Q from dS_out^T) and dQ (forward over dY, V, K from
-  // S_in^T) share d_a = dv: one launch, blockIdx.z selects the pass
+  // S_in^T) share d_a = dv: one launch
   MPassSet kq{};
   kq.p[0] = MPass{u(a.v), u(a.dy), u(a.q), static_cast<uint16_t*>(a.dk), a.dstate_out, nullptr, 1, 1, dk};
   kq.p[1] = MPass{u(a.dy), u(a.v), u(a.k), static_cast<uint16_t*>(a.dq), a.state_in, nullptr, 1, 0, dk};
-  launch_by_da(dv, kq, 2, dk, B, hd, H, g, T, s);
+  kq.npass = 2;
+  launch_by_da(dv, kq, dk, B, hd, H, g, T, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dV (reverse over K, Q, dY from dS_out); final state = dS_in.  After the dK
@@ -285,7 +303,8 @@ hipError_t launch_chunkwise_bwd_mfma(const BwdArgs& a, int B, int H, int T, int 
   MPassSet vs{};
   vs.p[0] = MPass{u(a.k), u(a.q), u(a.dy), static_cast<uint16_t*>(a.dv), a.dstate_out, a.dstate_in, 0, 1, dv};
   vs.p[1] = vs.p[0];
-  launch_by_da(dk, vs, 1, dv, B, hd, H, g, T, s);
+  vs.npass = 1;
+  launch_by_da(dk, vs, dv, B, hd, H, g, T, s);
   return hipGetLastError();
 }
 

@@ -2,11 +2,12 @@
 
     python -m retnet_retention_chunkwise_amd.rocprof_summary stats <kernel_stats.csv> [--cmd "..."]
     python -m retnet_retention_chunkwise_amd.rocprof_summary traffic --fetch <dir> --write <dir> \
-        --kernel <name substring> --source <kernel .hip> --copy-mib <N> [--cmd "..."]
+        --kernel <name substring>[,<substring>...] --source <kernel .hip> --copy-mib <N> [--cmd "..."]
 
 `stats` turns a `--kernel-trace --stats` kernel_stats.csv into a short text
 table.  `traffic` turns two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs into
-HBM bytes per launch of one kernel, calibrated against a plain copy of
+HBM bytes per launch of one kernel (or per call of several kernels, one
+dispatch of each, given as comma-separated name substrings), calibrated against a plain copy of
 `--copy-mib` MiB measured in the same runs (bytes = counter * known copy bytes /
 copy's counter), and records the sha256 of the kernel source so that a reader
 can tell whether the figures still describe the current kernel.
@@ -65,8 +66,18 @@ def _mean_for(entries, substr):
 def traffic(fetch_dir, write_dir, kernel, source, copy_mib, copy_substr="copy", cmd=""):
     f_entries = _per_dispatch(fetch_dir, "FETCH_SIZE")
     w_entries = _per_dispatch(write_dir, "WRITE_SIZE")
-    k_fetch, n_f = _mean_for(f_entries, kernel)
-    k_write, n_w = _mean_for(w_entries, kernel)
+    # a call made of several kernels (comma-separated substrings): one dispatch of each
+    parts = [k for k in kernel.split(",") if k]
+    k_fetch = k_write = 0.0
+    n_f, n_w = [], []
+    for part in parts:
+        m, n = _mean_for(f_entries, part)
+        k_fetch += m
+        n_f.append(str(n))
+        m, n = _mean_for(w_entries, part)
+        k_write += m
+        n_w.append(str(n))
+    n_f, n_w = "+".join(n_f), "+".join(n_w)
     c_fetch, _ = _mean_for(f_entries, copy_substr)
     c_write, _ = _mean_for(w_entries, copy_substr)
     copy_bytes = copy_mib * 1024 * 1024
