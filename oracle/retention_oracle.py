@@ -37,6 +37,7 @@ Functions
   recurrent_backward(q, k, v, gamma, dy, state_in, dstate_out)
                                             -- gradients of the recurrent form
                                                (chain rule; the pages give none)
+  group_norm(y, weight, bias, eps)          -- per-head GroupNorm of the output
 
 Tensors are torch tensors (any float dtype, any device is copied to the CPU)
 with layouts q, k: [B,H,T,d_k]; v: [B,H,T,d_v]; state: [B,H,d_k,d_v];
@@ -46,14 +47,15 @@ Parity status: every function above is pinned by tests/test_oracle.py against
 closed forms, a pure-Python brute force of the definition, and invariants;
 recurrent_backward against central finite differences of ``recurrent`` and
 the exact homogeneity identities of the operator (y is linear in q; y and the
-final state are linear in k, in v and in the initial state taken apart).
+final state are linear in k, in v and in the initial state taken apart);
+group_norm against torch's group_norm routine, hand values and invariants.
 """
 from __future__ import annotations
 
 import torch
 
 __all__ = ["recurrent", "recurrent_step", "parallel", "chunkwise", "chunk_state_contribution",
-           "recurrent_backward"]
+           "recurrent_backward", "group_norm"]
 
 
 def _f64(x: torch.Tensor) -> torch.Tensor:
@@ -239,3 +241,30 @@ def recurrent_backward(q, k, v, gamma, dy, state_in=None, dstate_out=None):
         gv[:, :, n, :] = torch.einsum("bhk,bhkv->bhv", k[:, :, n, :], G)
         carry = g * G                                                 # reaches S_(n-1)
     return gq, gk, gv, carry
+
+
+def group_norm(y, weight=None, bias=None, eps=1e-5):
+    """Per-head GroupNorm of the retention output.
+
+    The paperhub page (author answer A4, on the GroupNorm of Eq. 8) says that
+    multi-scale retention normalises with GroupNorm rather than LayerNorm
+    because different heads have different statistics: each head is one
+    group.  So for every (b, h, t) the d_v outputs of head h are normalised
+    together:
+        mu = mean_c y[c],  var = mean_c (y[c] - mu)^2   (biased, as GroupNorm)
+        out[c] = (y[c] - mu) / sqrt(var + eps) * weight[h, c] + bias[h, c]
+    weight, bias: per-channel affine [H, d_v] (None: 1 and 0).
+    y: [B,H,T,dv].  Returns float64 [B,H,T,dv].
+    """
+    y = _f64(y)
+    if y.dim() != 4:
+        raise ValueError("expected y [B,H,T,dv]")
+    H, dv = y.shape[1], y.shape[3]
+    mu = y.mean(dim=-1, keepdim=True)
+    var = ((y - mu) ** 2).mean(dim=-1, keepdim=True)
+    out = (y - mu) / torch.sqrt(var + float(eps))
+    if weight is not None:
+        out = out * _f64(weight).reshape(1, H, 1, dv)
+    if bias is not None:
+        out = out + _f64(bias).reshape(1, H, 1, dv)
+    return out

@@ -480,3 +480,73 @@ def test_backward_chunk_form_matches_transposed_passes():
     assert rel(rev(dv_r), gv) < 1e-12
     assert rel(rev(dk_r), gk) < 1e-12
     assert rel(gamma.view(1, 2, 1, 1) * h, gs) < 1e-12
+
+
+# ---------------------------------------------------------------- group norm
+def _group_norm_pins_fail(gn):
+    """True if a pin rejects the per-head GroupNorm candidate ``gn``."""
+    try:
+        # hand values: one head, d_v = 2, y = [1, 3]: mean 2, variance 1 -> [-1, 1]
+        # (eps = 0); two heads with different scales are normalised separately
+        y = torch.tensor([[[[1.0, 3.0]], [[10.0, 30.0]]]], dtype=torch.float64)
+        want = torch.tensor([[[[-1.0, 1.0]], [[-1.0, 1.0]]]], dtype=torch.float64)
+        if rel(gn(y, None, None, 0.0), want) > 1e-15:
+            return True
+        # torch's GroupNorm routine with one group per head over the H*d_v channels
+        gen = torch.Generator().manual_seed(51)
+        B, H, T, dv = 2, 3, 5, 7
+        y = torch.randn(B, H, T, dv, generator=gen, dtype=torch.float64) * 3 + 1
+        w = torch.randn(H, dv, generator=gen, dtype=torch.float64)
+        b = torch.randn(H, dv, generator=gen, dtype=torch.float64)
+        x = y.permute(0, 2, 1, 3).reshape(B * T, H * dv)
+        ref = torch.nn.functional.group_norm(x, H, w.reshape(-1), b.reshape(-1), eps=1e-3)
+        ref = ref.reshape(B, T, H, dv).permute(0, 2, 1, 3)
+        if rel(gn(y, w, b, 1e-3), ref) > 1e-13:
+            return True
+        # invariants: a constant shift per group changes nothing; without the
+        # affine the group variance is var / (var + eps)
+        shift = torch.randn(B, H, T, 1, generator=gen, dtype=torch.float64)
+        if rel(gn(y + shift, w, b, 1e-3), gn(y, w, b, 1e-3)) > 1e-12:
+            return True
+        o = gn(y, None, None, 0.5)
+        v = y.var(dim=-1, unbiased=False, keepdim=True)
+        if rel(o.var(dim=-1, unbiased=False, keepdim=True), v / (v + 0.5)) > 1e-12:
+            return True
+    except Exception:
+        return True
+    return False
+
+
+def test_group_norm_pins_accept_the_oracle():
+    assert not _group_norm_pins_fail(oracle.group_norm)
+
+
+def _group_norm_mutant(kind):
+    def run(y, w=None, b=None, eps=1e-5):
+        y = y.double()
+        H, dv = y.shape[1], y.shape[3]
+        if kind == "layer_norm_over_heads":
+            yy = y.permute(0, 2, 1, 3).reshape(y.shape[0], y.shape[2], H * dv)
+            mu = yy.mean(-1, keepdim=True)
+            var = yy.var(-1, unbiased=False, keepdim=True)
+            out = ((yy - mu) / torch.sqrt(var + eps)).reshape(y.shape[0], y.shape[2], H, dv).permute(0, 2, 1, 3)
+        else:
+            mu = y.mean(-1, keepdim=True)
+            var = y.var(-1, unbiased=(kind == "unbiased_variance"), keepdim=True)
+            if kind == "eps_outside_sqrt":
+                out = (y - mu) / (torch.sqrt(var) + eps)
+            else:
+                out = (y - mu) / torch.sqrt(var + eps)
+        if w is not None:
+            ww = w.double().reshape(1, H, 1, dv)
+            out = out * (ww.mean(-1, keepdim=True) if kind == "affine_per_head" else ww)
+        if b is not None:
+            out = out + b.double().reshape(1, H, 1, dv)
+        return out
+    return run
+
+
+@pytest.mark.parametrize("kind", ["layer_norm_over_heads", "unbiased_variance", "eps_outside_sqrt",
+                                  "affine_per_head"])
+def test_group_norm_pins_reject_planted_mistakes(kind):
+    assert _group_norm_pins_fail(_group_norm_mutant(kind)), kind
