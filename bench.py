@@ -13,7 +13,8 @@ The recurrent decode step (retention_recurrent_step, batch 128, H=16, fp32
 256x512 state per head, 1000 chained steps) is measured in the same run and
 reported in the "decode" object, and a chunkwise continuation of 16 new tokens
 per stream from that state (the short-block streaming kernel) in the
-"continuation" object.
+"continuation" object, the backward of the chunkwise workload in "backward"
+and the per-head GroupNorm of its output in "group_norm".
 
 Prints ONE JSON line.  "value" is whole-job throughput over the timed loop.
 The roofline of the chunkwise kernel uses algorithmic HBM bytes (bf16 Q, K, V
@@ -262,6 +263,27 @@ def main():
     del bq, bk, bv, bs0, bdy, bds
     torch.cuda.empty_cache()
 
+    # ------------------------------------------- per-head GroupNorm (layer1p3b y)
+    gy = [torch.randn(wl.B, wl.H, wl.T, wl.dv, device=dev).to(torch.bfloat16) for _ in range(4)]
+    gw = torch.randn(wl.H, wl.dv, device=dev)
+    gb = torch.randn(wl.H, wl.dv, device=dev)
+    gout = torch.empty_like(gy[0])
+    for i in range(3):
+        ret.group_norm(gy[i % 4], gw, gb, 1e-5, out=gout)
+    torch.cuda.synchronize()
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for i, (a, b) in enumerate(gev):
+        a.record(stream)
+        ret.group_norm(gy[i % 4], gw, gb, 1e-5, out=gout)
+        b.record(stream)
+    torch.cuda.synchronize()
+    gn_us = statistics.median(a.elapsed_time(b) for a, b in gev) * 1e3
+    gn_bytes = 2 * head_tokens * wl.dv * 2 + 2 * wl.H * wl.dv * 4  # y in, out out (bf16); weight, bias
+    gn_src = os.path.join(ROOT, "retnet_retention_chunkwise_amd", "csrc", "group_norm.hip")
+    gn_traffic = load_traffic("group_norm_layer1p3b_traffic.txt", gn_src)
+    del gy, gw, gb, gout
+    torch.cuda.empty_cache()
+
     out = {
         "metric": "retention tokens/sec (chunkwise fwd) + decode steps/sec; % MFMA / HBM peak",
         "value": value,
@@ -323,6 +345,13 @@ def main():
                      "algorithmic_flops_per_launch": bwd_flops,
                      "mfma_tflops": bwd_flops / (bwd_us * 1e-6) / 1e12,
                      "mfma_frac": bwd_flops / (bwd_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS},
+    }
+    out["group_norm"] = {
+        "workload": "per-head GroupNorm of a layer1p3b output: [4,8,2048,512] bf16, affine weight/bias, 4 rotating inputs",
+        "kernel_us": gn_us,
+        "roofline": {"bound": "hbm", "achieved": gn_bytes / (gn_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": gn_bytes / (gn_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": gn_traffic, "algorithmic_bytes_per_launch": gn_bytes},
     }
     if not args.no_cpu_baseline:
         sample_B = int(os.environ.get("RET_CPU_SAMPLE_B", str(wl.B)))

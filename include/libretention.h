@@ -134,6 +134,23 @@ ret_status retention_chunkwise_bwd(const void* q, const void* k, const void* v, 
                                    int T, int dk, int dv, int C, ret_dtype dt, void* stream);
 
 /*
+ * Per-head GroupNorm of a retention output: every head is one group (the
+ * paperhub page, author answer A4: GroupNorm rather than LayerNorm because the
+ * heads have different statistics).  For each (b, h, t), over c = 0..dv-1:
+ *   mu = mean_c y, var = mean_c (y - mu)^2 (biased),
+ *   out[c] = (y[c] - mu) / sqrt(var + eps) * weight[h][c] + bias[h][c].
+ * The gate that follows it in a retention layer is not part of this call.
+ *   y      : [B,H,T,dv] in dt (the layout retention_*_fwd write).
+ *   weight : nullable (ones); device fp32 [H,dv].  bias : nullable (zeros); device fp32 [H,dv].
+ *   eps    : finite, >= 0.
+ *   out    : written, [B,H,T,dv] in dt; may be y exactly (in place), must not
+ *            overlap it otherwise, nor weight or bias.
+ * fp32 arithmetic; the output is rounded to dt.
+ */
+ret_status retention_group_norm(const void* y, const float* weight, const float* bias, float eps, void* out, int B,
+                                int H, int T, int dv, ret_dtype dt, void* stream);
+
+/*
  * One recurrent (decode) step, in place on the state: S <- gamma S + k^T v,
  * then y = q S (the new state, so the current token is included).  This is the
  * recurrent form of the aimpact page ("Il meccanismo"); the baulab page

@@ -8,6 +8,7 @@ The compute lives in hand-written HIP kernels behind a C ABI
         -> (grad_q, grad_k, grad_v, grad_state_in)
     parallel_fwd(q, k, v, gamma, state_in=None) -> y
     recurrent_step(q, k, v, gamma, state) -> y          (state updated in place)
+    group_norm(y, weight=None, bias=None, eps=1e-5) -> out   (per-head GroupNorm of y)
 
 Build the library with ``python -m retnet_retention_chunkwise_amd.build``.
 """
@@ -20,6 +21,7 @@ from ._lib import (  # noqa: F401
     chunkwise_bwd,
     chunkwise_fwd,
     chunkwise_workspace_bytes,
+    group_norm,
     last_error,
     load,
     parallel_fwd,

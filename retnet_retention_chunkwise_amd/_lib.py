@@ -28,6 +28,7 @@ SIGNATURES = {
     "retention_chunkwise_fwd": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "retention_chunkwise_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "retention_recurrent_step": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "retention_group_norm": (_i, [_vp, _vp, _vp, ctypes.c_float, _vp, _i, _i, _i, _i, _i, _vp]),
     "retention_chunkwise_bwd": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
                                      _i, _vp]),
     "retention_last_error": (ctypes.c_char_p, []),
@@ -212,6 +213,35 @@ def chunkwise_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma, C: i
                                      _ptr(grad_state_in), B, H, T, dk, dv, int(C), dt, _stream(q.device))
     _check(st)
     return gq, gk, gv, grad_state_in
+
+
+def group_norm(y: torch.Tensor, weight: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+               eps: float = 1e-5, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-head GroupNorm of a [B,H,T,dv] retention output (retention_group_norm).
+
+    weight, bias: optional fp32 [H,dv] device tensors.  out: a tensor to fill
+    (may be y itself), or None to allocate one.
+    """
+    lib = load()
+    _dev(y, "y")
+    if y.dim() != 4:
+        raise ValueError("expected y [B,H,T,dv]")
+    B, H, T, dv = y.shape
+    dt = _dt(y)
+    for t, n in ((weight, "weight"), (bias, "bias")):
+        if t is not None:
+            _dev(t, n)
+            if t.dtype != torch.float32 or tuple(t.shape) != (H, dv) or t.device != y.device:
+                raise ValueError(f"{n} must be float32 ({H}, {dv}) on {y.device}")
+    if out is None:
+        out = torch.empty_like(y)
+    else:
+        _dev(out, "out")
+        if out.shape != y.shape or out.dtype != y.dtype or out.device != y.device:
+            raise ValueError("out must match y")
+    _check(lib.retention_group_norm(_ptr(y), _ptr(weight), _ptr(bias), float(eps), _ptr(out), B, H, T, dv, dt,
+                                    _stream(y.device)))
+    return out
 
 
 def parallel_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma,

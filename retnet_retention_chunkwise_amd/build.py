@@ -31,6 +31,7 @@ SOURCES = [
     "short_chunk.hip",
     "chunkwise_bwd.hip",
     "chunkwise_bwd_mfma.hip",
+    "group_norm.hip",
 ]
 
 ARCH = "gfx950"

@@ -260,4 +260,32 @@ ret_status retention_chunkwise_bwd(const void* q, const void* k, const void* v, 
   });
 }
 
+ret_status retention_group_norm(const void* y, const float* weight, const float* bias, float eps, void* out, int B,
+                                int H, int T, int dv, ret_dtype dt, void* stream) {
+  const char* fn = "retention_group_norm";
+  if (B < 1 || H < 1) return fail(RET_ERR_INVALID_ARG, "%s: B=%d and H=%d must be >= 1", fn, B, H);
+  if (T < 0) return fail(RET_ERR_INVALID_ARG, "%s: T=%d must be >= 0", fn, T);
+  if (dv < 1) return fail(RET_ERR_INVALID_ARG, "%s: dv=%d must be >= 1", fn, dv);
+  if (dt != RET_F32 && dt != RET_BF16)
+    return fail(RET_ERR_UNSUPPORTED, "%s: dtype %d is not RET_F32 or RET_BF16", fn, static_cast<int>(dt));
+  if (dv > RET_MAX_DV) return fail(RET_ERR_UNSUPPORTED, "%s: dv=%d exceeds %d", fn, dv, RET_MAX_DV);
+  if (!std::isfinite(eps) || eps < 0.0f)
+    return fail(RET_ERR_INVALID_ARG, "%s: eps = %g must be finite and >= 0", fn, static_cast<double>(eps));
+  const long long n = static_cast<long long>(B) * H * T * dv;
+  if (n > kMaxElems) return fail(RET_ERR_UNSUPPORTED, "%s: y has 2^31 or more elements", fn);
+  if (T > 0 && (y == nullptr || out == nullptr)) return fail(RET_ERR_INVALID_ARG, "%s: y and out are required", fn);
+  if (misaligned(y) || misaligned(out) || misaligned(weight) || misaligned(bias))
+    return fail(RET_ERR_UNSUPPORTED, "%s: tensor pointers must be 16-byte aligned", fn);
+  const size_t ny = static_cast<size_t>(n) * dsize(dt);
+  const size_t nw = static_cast<size_t>(H) * dv * 4;
+  if (out != y && overlap(out, ny, y, ny))
+    return fail(RET_ERR_INVALID_ARG, "%s: out overlaps y without being the same buffer", fn);
+  if (overlap(out, ny, weight, nw) || overlap(out, ny, bias, nw))
+    return fail(RET_ERR_INVALID_ARG, "%s: out overlaps weight or bias", fn);
+  if (T == 0) return ok();
+  const hipError_t e = ret::launch_group_norm(y, weight, bias, eps, out, B, H, T, dv, static_cast<int>(dt),
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(fn, e);
+}
+
 }  // extern "C"

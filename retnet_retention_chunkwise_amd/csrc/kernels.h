@@ -79,6 +79,10 @@ bool chunkwise_bwd_mfma_supports(int dk, int dv, int dt);
 hipError_t launch_chunkwise_bwd_mfma(const BwdArgs& a, int B, int H, int T, int dk, int dv, const HeadGroup& g,
                                      hipStream_t s);
 
+// Per-head GroupNorm of a [B,H,T,dv] output (dt: 0 = fp32, 1 = bf16); out may be y.
+hipError_t launch_group_norm(const void* y, const float* weight, const float* bias, float eps, void* out, int B,
+                             int H, int T, int dv, int dt, hipStream_t s);
+
 // Copies state_in (or zeros when null) into state_out: the T = 0 case.
 hipError_t launch_state_copy(const float* state_in, float* state_out, size_t n, hipStream_t s);
 

@@ -219,3 +219,50 @@ def test_host_dispatch_of_every_backward_parity_shape_without_a_device(lib):
         st = lib.retention_chunkwise_bwd(ptrs[0], ptrs[1], ptrs[2], gam(*([0.5] * H)), None, ptrs[3], None,
                                          ptrs[4], ptrs[5], ptrs[6], None, B, H, T, dk, dv, C, d, None)
         assert st == 3, (B, H, T, dk, dv, C, dt, _lib.last_error())
+
+
+def gn(lib, y=ctypes.c_void_p(0x100000), w=None, b=None, eps=1e-5, out=ctypes.c_void_p(0x200000), B=1, H=2, T=8,
+       dv=16, dt=0):
+    return lib.retention_group_norm(y, w, b, eps, out, B, H, T, dv, dt, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(B=0), INVALID, "B=0"),
+    (dict(T=-1), INVALID, "T=-1"),
+    (dict(dv=0), INVALID, "dv=0"),
+    (dict(dv=513), UNSUPPORTED, "exceeds"),
+    (dict(dt=2), UNSUPPORTED, "dtype"),
+    (dict(eps=-1.0), INVALID, "eps"),
+    (dict(eps=float("nan")), INVALID, "eps"),
+    (dict(y=None), INVALID, "required"),
+    (dict(out=FAKE_MIS), UNSUPPORTED, "aligned"),
+    (dict(out=ctypes.c_void_p(0x100010)), INVALID, "overlaps y"),
+    (dict(w=ctypes.c_void_p(0x200000)), INVALID, "weight or bias"),
+])
+def test_group_norm_rejects(lib, kw, status, needle):
+    assert gn(lib, **kw) == status
+    assert needle in _lib.last_error(), _lib.last_error()
+
+
+def test_group_norm_empty_and_in_place_pass_validation(lib):
+    """T = 0 is a no-op; out == y is accepted (with no device the call then
+    fails only at the launch; skipped where a GPU is visible)."""
+    assert gn(lib, T=0) == _lib.RET_OK
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("placeholder pointers must never reach a real device")
+    assert gn(lib, out=ctypes.c_void_p(0x100000)) == 3
+
+
+def test_host_dispatch_of_every_group_norm_parity_shape_without_a_device(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("placeholder pointers must never reach a real device")
+    import test_parity_gpu as parity
+    for (B, H, T, dv, dt, affine, eps, in_place) in parity.GN_CASES:
+        d = 1 if dt == "bf16" else 0
+        y = ctypes.c_void_p(1 << 36)
+        out = y if in_place else ctypes.c_void_p(2 << 36)
+        w = ctypes.c_void_p(3 << 36) if affine else None
+        b = ctypes.c_void_p(4 << 36) if affine else None
+        assert lib.retention_group_norm(y, w, b, eps, out, B, H, T, dv, d, None) == 3, _lib.last_error()

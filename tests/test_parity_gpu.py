@@ -236,6 +236,53 @@ def test_chunkwise_bwd_in_place_state_gradient_and_empty_sequence():
     assert torch.equal(gsi.cpu(), ds)
 
 
+# --------------------------------------------------------------- group norm
+GN_CASES = [
+    # B, H, T, dv, dtype, affine, eps, in_place
+    (2, 3, 100, 512, "bf16", True, 1e-5, False),
+    (1, 2, 77, 64, "f32", True, 1e-5, True),
+    (1, 4, 33, 300, "bf16", False, 1e-3, False),
+    (1, 1, 5, 7, "f32", True, 0.0, False),
+    (2, 130, 3, 16, "f32", False, 1e-5, True),
+    (1, 2, 40, 256, "f32", True, 1e-6, False),
+    (1, 2, 9, 100, "f32", True, 1e-5, False),
+]
+
+
+@pytest.mark.parametrize("B,H,T,dv,dt,affine,eps,in_place", GN_CASES)
+def test_group_norm_vs_oracle(B, H, T, dv, dt, affine, eps, in_place):
+    say(f"group norm B{B} H{H} T{T} dv{dv} {dt} affine={affine} eps={eps} in_place={in_place}")
+    gen = torch.Generator().manual_seed(60)
+    y = (torch.randn(B, H, T, dv, generator=gen) * 2.0 + 0.5).to(torch.bfloat16 if dt == "bf16" else torch.float32)
+    w = torch.randn(H, dv, generator=gen) if affine else None
+    b = torch.randn(H, dv, generator=gen) if affine else None
+    ref = oracle.group_norm(y, w, b, eps)
+    yd, wd, bd = to_dev(y, w, b)
+    out = ret.group_norm(yd, wd, bd, eps, out=yd if in_place else None)
+    torch.cuda.synchronize()
+    check("group norm", out, ref, tol(y.dtype))
+
+
+def test_group_norm_of_chunkwise_output_at_layer_size():
+    """The chunkwise forward followed by the per-head GroupNorm at the 1.3B-scale
+    layer shape, sampled heads against the oracle."""
+    wl = WORKLOADS["layer1p3b"]
+    say("chunkwise + group norm at layer size")
+    q, k, v = make_inputs(wl.B, wl.H, wl.T, wl.dk, wl.dv, wl.dtype, seed=61)
+    gen = torch.Generator().manual_seed(62)
+    w = torch.randn(wl.H, wl.dv, generator=gen)
+    b = torch.randn(wl.H, wl.dv, generator=gen)
+    qd, kd, vd, wd, bd = to_dev(q, k, v, w, b)
+    y, _ = ret.chunkwise_fwd(qd, kd, vd, list(wl.gammas), wl.C, state_out=False)
+    out = ret.group_norm(y, wd, bd, 1e-5)
+    torch.cuda.synchronize()
+    for bb, h in ((0, 0), (2, 5)):
+        sl = lambda t: t[bb:bb + 1, h:h + 1]
+        y_ref, _ = oracle.recurrent(sl(q), sl(k), sl(v), torch.tensor([wl.gammas[h]]))
+        ref = oracle.group_norm(y_ref, w[h:h + 1], b[h:h + 1], 1e-5)
+        check(f"group norm of y (b{bb} h{h})", sl(out), ref, tol(q.dtype))
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_parallel_vs_oracle(dt):
     B, H, T, dk, dv = 2, 3, 150, 32, 64
