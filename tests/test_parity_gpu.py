@@ -441,6 +441,38 @@ def test_deterministic_reruns():
     assert torch.equal(y1, y2) and torch.equal(s1, s2)
 
 
+def test_chunkwise_in_a_captured_graph_matches_eager():
+    """Launches captured in a HIP graph (as the benchmark issues them) give the
+    eager result bit for bit on every replay, with eager work and
+    synchronisations between the replays."""
+    say("chunkwise forward and backward captured in a graph, replayed 3 times")
+    B, H, T, dk, dv, C = 2, 4, 300, 256, 512, 64
+    q, k, v, s0 = to_dev(*make_inputs(B, H, T, dk, dv, "bf16", seed=12, with_state=True))
+    dy = torch.randn(B, H, T, dv, device=DEV).div_(16).to(torch.bfloat16)
+    gs = gammas_for(H, 0.9)
+    y_eager, s_eager = ret.chunkwise_fwd(q, k, v, gs, C, state_in=s0)
+    g_eager = ret.chunkwise_bwd(q, k, v, gs, C, dy, state_in=s0)
+    y = torch.empty_like(y_eager)
+    s = torch.empty_like(s_eager)
+    gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    gsi = torch.empty_like(s0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ret.chunkwise_fwd(q, k, v, gs, C, state_in=s0, state_out=s, y=y)
+        out = ret.chunkwise_bwd(q, k, v, gs, C, dy, state_in=s0, grad_state_in=gsi)
+    for rep in range(3):
+        y.zero_()
+        s.zero_()
+        gsi.zero_()
+        graph.replay()
+        other, _ = ret.chunkwise_fwd(v[:, :, :, :dk].contiguous(), k, v, gs, C)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager) and torch.equal(s, s_eager), rep
+        for a, b in zip(out, g_eager):
+            assert torch.equal(a, b), rep
+
+
 # ------------------------------------------------------- full-size workloads
 def sampled_heads(B, H):
     return sorted({(0, 0), (B // 2, H // 2), (B - 1, H - 1)})
