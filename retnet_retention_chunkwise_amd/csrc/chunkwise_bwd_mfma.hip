@@ -12,21 +12,25 @@
 //   dK: reverse, (V, dY, Q), S_0 = dS_out^T
 //   dV: reverse, (K, Q, dY), S_0 = dS_out; the final S is dS_in.
 //
-// Work decomposition: a workgroup (4 waves) owns one (batch, head, tile of 64
-// X columns) and walks the 32-token chunks in order.  Wave w owns 16 columns
-// of the tile and keeps ALL d_a rows of their state in MFMA accumulator layout
-// (lane: column l%16, rows 4(l/16)+i of each 16-row block), so no state ever
-// goes through LDS:
-//   * the cross term is formed transposed, Out^T = S^T A^T: the accumulator
-//     layout of S, read as an MFMA A operand, covers the features
-//     {32s + 4g + i, 32s + 16 + 4g + i} of lane group g, and the matching B
-//     operand is two 8-byte reads of the A rows in LDS (the same feature
-//     permutation on both sides of the contraction);
-//   * the scores P = (A B^T) .* mask are one 16x16 tile per wave, written to
-//     LDS in bf16, and the intra term Out^T += X^T P^T reads X^T with the
-//     transposing LDS load;
-//   * the update S <- gamma^L S + B^T (z X) accumulates straight into the
-//     state registers, B^T and z X through the transposing load.
+// Work decomposition: a workgroup owns one (batch, head, tile of 64 X
+// columns) and walks the 32-token chunks in order.  It has 4 column strips of
+// 16 columns times KS parts of d_a (KS = 4, or 2 for d_a = 64): wave (strip,
+// part) keeps the d_a/KS state rows of its part for its 16 columns in MFMA
+// accumulator layout (lane: column l%16, rows 4(l/16)+i of each 16-row
+// block), so no state goes through LDS, and KS waves per SIMD hide each
+// other's latency:
+//   * the cross term is formed transposed, Out^T = S^T A^T, each wave over its
+//     part of d_a: the accumulator layout of S, read as an MFMA A operand,
+//     covers the features {32s + 4g + i, 32s + 16 + 4g + i} of lane group g,
+//     and the matching B operand is two 8-byte reads of the A rows in LDS (the
+//     same feature permutation on both sides of the contraction).  Parts
+//     1..KS-1 hand their partial sums to part 0 through LDS (across the
+//     barrier that also publishes the scores);
+//   * the scores P = (A B^T) .* mask are one 16x16 tile per wave of part 1,
+//     written to LDS in bf16; part 0 adds the intra term Out^T += X^T P^T (X^T
+//     through the transposing LDS load) and stores;
+//   * every wave updates its rows, S <- gamma^L S + B^T (z X), straight into
+//     the state registers, B^T and z X through the transposing load.
 // Out^T leaves each lane 4 consecutive columns of one token: 8-byte stores.
 // In the operands read with the transposing load (X^T, B^T, z X), k index
 // 8g + e of lane group g stands for token 4g + (e % 4) + 16 (e / 4) (P^T is
@@ -45,8 +49,7 @@ namespace ret {
 namespace {
 
 constexpr int kCT = 32;        // tokens per chunk
-constexpr int kTX = 64;        // X / Out columns per workgroup (16 per wave)
-constexpr int kThreads = 256;  // 4 waves
+constexpr int kTX = 64;        // X / Out columns per workgroup (16 per wave pair)
 
 struct MPass {
   const uint16_t* a;  // [BH, T, DA] bf16
@@ -66,27 +69,30 @@ struct MPassSet {
 
 template <int DA>
 struct BCfg {
+  // waves per column strip, each owning DA / KS state rows (a k-step of 32
+  // features needs two 16-row blocks per wave)
+  static constexpr int KS = DA >= 128 ? 4 : 2;
+  static constexpr int NT = 256 * KS;   // threads: 4 column strips x KS parts of d_a
   static constexpr int ALD = DA + 8;    // bf16 row stride of the A tile in LDS
   static constexpr int BLD = DA + 16;   // row stride of the B tile
   static constexpr int XLD = kTX + 16;  // row stride of the X and zX tiles
   static constexpr int PLD = kCT + 8;   // row stride of the score tile
-  static constexpr int NAB = DA / 16;   // 16-row state blocks per wave
-  static constexpr int NS = DA / 32;    // 32-wide k-steps over d_a
-  static constexpr int NLD = kCT * DA / 8 / kThreads;  // 16-byte loads of A (and of B) per thread
-  static_assert(NLD >= 1 && kCT * DA / 8 % kThreads == 0, "A/B tile split");
+  static constexpr int NABH = DA / 16 / KS;  // 16-row state blocks per wave (its part of d_a)
+  static constexpr int NSH = DA / 32 / KS;   // 32-wide k-steps per wave
+  static constexpr int NP = kCT * DA / 8;                        // 16-byte pieces of the A (and B) tile
+  static constexpr int NLD = (NP + NT - 1) / NT;                 // per thread
 };
 
-// d_a = 512 keeps 128 state registers per lane and takes the whole register
-// file (one workgroup per CU); smaller d_a leave room for two.
 template <int DA>
-__global__ __launch_bounds__(kThreads, DA >= 512 ? 1 : 2) void bwd_pass_mfma_kernel(MPassSet ps, HeadDecay gam,
-                                                                                     int H, int h0, int nh, int Tn) {
+__global__ __launch_bounds__(BCfg<DA>::NT) void bwd_pass_mfma_kernel(MPassSet ps, HeadDecay gam, int H, int h0, int nh,
+                                                                 int Tn) {
   using F = BCfg<DA>;
   __shared__ __attribute__((aligned(16))) uint16_t As[kCT * F::ALD];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[kCT * F::BLD];
   __shared__ __attribute__((aligned(16))) uint16_t Xs[kCT * F::XLD];
   __shared__ __attribute__((aligned(16))) uint16_t Zs[kCT * F::XLD];
   __shared__ __attribute__((aligned(16))) uint16_t Ps[kCT * F::PLD];
+  __shared__ f32x4 Xch[F::KS - 1][4][2][64];  // cross-term partials of parts 1..KS-1
 
   // Work item.  Workgroup ids are dealt round-robin over the 8 XCDs; the
   // remap gives each XCD a contiguous range of items, so the column tiles and
@@ -104,6 +110,8 @@ __global__ __launch_bounds__(kThreads, DA >= 512 ? 1 : 2) void bwd_pass_mfma_ker
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int cs = w & 3;      // column strip
+  const int hf = w >> 2;     // d_a part: state rows [hf DA/KS, (hf+1) DA/KS)
   const int g = lane >> 4;   // lane group
   const int lr = lane & 15;  // lane within the group
   const int hl = hitem % nh;
@@ -111,7 +119,7 @@ __global__ __launch_bounds__(kThreads, DA >= 512 ? 1 : 2) void bwd_pass_mfma_ker
   const long head = static_cast<long>(bb) * H + h0 + hl;
   const float lg = gam.log2g[hl];
   const int c0 = tile * kTX;
-  const int cw = 16 * w;  // this wave's columns inside the tile
+  const int cw = 16 * cs;  // this wave's columns inside the tile
 
   const rsrc_t ra = make_rsrc(p.a + head * Tn * DA, static_cast<uint32_t>(Tn) * DA * 2);
   const rsrc_t rb = make_rsrc(p.b + head * Tn * DA, static_cast<uint32_t>(Tn) * DA * 2);
@@ -119,13 +127,13 @@ __global__ __launch_bounds__(kThreads, DA >= 512 ? 1 : 2) void bwd_pass_mfma_ker
   const rsrc_t ro = make_rsrc(p.out + head * Tn * DX, static_cast<uint32_t>(Tn) * DX * 2);
   const long sb = head * static_cast<long>(DA) * DX;
 
-  // state: S[16 ab + 4 g + i][c0 + cw + lr] in Sacc[ab][i]
-  f32x4 Sacc[F::NAB];
+  // state: S[16 (hf NABH + l) + 4 g + i][c0 + cw + lr] in Sacc[l][i]
+  f32x4 Sacc[F::NABH];
   {
     const int x = c0 + cw + lr;
 #pragma unroll
-    for (int ab = 0; ab < F::NAB; ++ab) {
-      const int a = 16 * ab + 4 * g;
+    for (int l = 0; l < F::NABH; ++l) {
+      const int a = 16 * (hf * F::NABH + l) + 4 * g;
       f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
       if (p.s0 != nullptr) {
         if (p.s0_t) {
@@ -135,23 +143,27 @@ __global__ __launch_bounds__(kThreads, DA >= 512 ? 1 : 2) void bwd_pass_mfma_ker
           for (int i = 0; i < 4; ++i) v[i] = p.s0[sb + static_cast<long>(a + i) * DX + x];
         }
       }
-      Sacc[ab] = v;
+      Sacc[l] = v;
     }
   }
 
-  // staging map: A/B piece r of this thread = row (tid + 256 r) / (DA/8), 8 features
+  // staging map: A/B piece q = tid + 512 r (q < NP) = row q / (DA/8), 8 features;
+  // X piece of threads 0..255: row tid / 8, columns 8 (tid % 8) .. +7 of the tile
   constexpr int PPR = DA / 8;  // 16-byte pieces per row
   u32x4 pa[F::NLD], pb[F::NLD], px;
-  const int xj = tid >> 3, xc = (tid & 7) * 8;  // X piece: row xj, columns xc..xc+7 of the tile
+  const bool xthr = tid < kCT * kTX / 8;
+  const int xj = (tid >> 3) & (kCT - 1), xc = (tid & 7) * 8;
   auto prefetch = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < F::NLD; ++r) {
-      const int q = tid + kThreads * r;
-      const uint32_t off = (static_cast<uint32_t>(t0 + q / PPR) * DA + (q % PPR) * 8) * 2;
-      pa[r] = buffer_load16(ra, off);
-      pb[r] = buffer_load16(rb, off);
+      const int q = tid + F::NT * r;
+      if (q < F::NP) {
+        const uint32_t off = (static_cast<uint32_t>(t0 + q / PPR) * DA + (q % PPR) * 8) * 2;
+        pa[r] = buffer_load16(ra, off);
+        pb[r] = buffer_load16(rb, off);
+      }
     }
-    px = buffer_load16(rx, (static_cast<uint32_t>(t0 + xj) * DX + c0 + xc) * 2);
+    if (xthr) px = buffer_load16(rx, (static_cast<uint32_t>(t0 + xj) * DX + c0 + xc) * 2);
   };
 
   const int nch = (Tn + kCT - 1) / kCT;
@@ -164,11 +176,13 @@ __global__ __launch_bounds__(kThreads, DA >= 512 ? 1 : 2) void bwd_pass_mfma_ker
     // ---- stage this chunk (the previous chunk ended with a barrier)
 #pragma unroll
     for (int r = 0; r < F::NLD; ++r) {
-      const int q = tid + kThreads * r;
-      *reinterpret_cast<u32x4*>(&As[(q / PPR) * F::ALD + (q % PPR) * 8]) = pa[r];
-      *reinterpret_cast<u32x4*>(&Bs[(q / PPR) * F::BLD + (q % PPR) * 8]) = pb[r];
+      const int q = tid + F::NT * r;
+      if (q < F::NP) {
+        *reinterpret_cast<u32x4*>(&As[(q / PPR) * F::ALD + (q % PPR) * 8]) = pa[r];
+        *reinterpret_cast<u32x4*>(&Bs[(q / PPR) * F::BLD + (q % PPR) * 8]) = pb[r];
+      }
     }
-    {
+    if (xthr) {
       *reinterpret_cast<u32x4*>(&Xs[xj * F::XLD + xc]) = px;
       const float z = xj < L ? gamma_pow(lg, rev ? xj + 1 : L - 1 - xj) : 0.0f;
       const bf16x8 xv = __builtin_bit_cast(bf16x8, px);
@@ -180,14 +194,15 @@ __global__ __launch_bounds__(kThreads, DA >= 512 ? 1 : 2) void bwd_pass_mfma_ker
     if (it + 1 < nch) prefetch((rev ? ci - 1 : ci + 1) * kCT);
     lds_barrier();
 
-    // ---- scores: tile (jb, jpb) of wave w, masked and decayed, to LDS in bf16
-    {
-      const int jb = w >> 1, jpb = w & 1;
+    // ---- scores (waves of the upper half): tile (jb, jpb) = strip cs, masked
+    // and decayed, to LDS in bf16
+    if (hf == 1) {
+      const int jb = cs >> 1, jpb = cs & 1;
       const bool live = rev ? jpb >= jb : jpb <= jb;
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
       if (live) {
 #pragma unroll
-        for (int s = 0; s < F::NS; ++s) {
+        for (int s = 0; s < DA / 32; ++s) {
           const bf16x8 av = lds_read16(&As[(16 * jb + lr) * F::ALD + 32 * s + 8 * g]);
           const bf16x8 bv = lds_read16(&Bs[(16 * jpb + lr) * F::BLD + 32 * s + 8 * g]);
           acc = mfma(av, bv, acc);
@@ -202,15 +217,15 @@ __global__ __launch_bounds__(kThreads, DA >= 512 ? 1 : 2) void bwd_pass_mfma_ker
         Ps[j * F::PLD + jp] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(val));
       }
     }
-    lds_barrier();
 
-    // ---- outputs: Out^T = diag-scaled S^T A^T + X^T P^T, two 16-token blocks
+    // ---- cross term over this wave's half of d_a: Out^T = S^T A^T (partial)
     f32x4 O[2];
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) O[jb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int s = 0; s < F::NS; ++s) {
-      const bf16x8 sv = pack_bf16x8(Sacc[2 * s], Sacc[2 * s + 1]);
+    for (int sl = 0; sl < F::NSH; ++sl) {
+      const int s = hf * F::NSH + sl;
+      const bf16x8 sv = pack_bf16x8(Sacc[2 * sl], Sacc[2 * sl + 1]);
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
         const uint16_t* row = &As[(16 * jb + lr) * F::ALD + 32 * s + 4 * g];
@@ -218,13 +233,22 @@ __global__ __launch_bounds__(kThreads, DA >= 512 ? 1 : 2) void bwd_pass_mfma_ker
         O[jb] = mfma(sv, av, O[jb]);
       }
     }
-    {
+    if (hf >= 1) {
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) Xch[hf - 1][cs][jb][lane] = O[jb];
+    }
+    lds_barrier();  // scores and upper partials are in LDS
+
+    // ---- outputs (lower half): add the partner's partial, scale, + X^T P^T
+    if (hf == 0) {
       const uint16_t* xr = &Xs[(4 * g + (lr >> 2)) * F::XLD + cw + 4 * (lr & 3)];
       const bf16x8 xt = join(lds_read_tr(xr), lds_read_tr(xr + 16 * F::XLD));
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
         const int j = 16 * jb + lr;
         const float wj = j < L ? gamma_pow(lg, rev ? L - 1 - j : j + 1) : 0.0f;
+#pragma unroll
+        for (int u = 0; u < F::KS - 1; ++u) O[jb] += Xch[u][cs][jb][lane];
         O[jb] *= wj;
         const bf16x8 pv = join(*reinterpret_cast<const s16x4*>(&Ps[j * F::PLD + 4 * g]),
                                *reinterpret_cast<const s16x4*>(&Ps[j * F::PLD + 16 + 4 * g]));
@@ -238,16 +262,16 @@ __global__ __launch_bounds__(kThreads, DA >= 512 ? 1 : 2) void bwd_pass_mfma_ker
       }
     }
 
-    // ---- state update: S <- gamma^L S + B^T (z X)
+    // ---- state update of this wave's rows: S <- gamma^L S + B^T (z X)
     {
       const float gL = L == kCT ? gL_full : gamma_pow(lg, L);
       const uint16_t* zr = &Zs[(4 * g + (lr >> 2)) * F::XLD + cw + 4 * (lr & 3)];
       const bf16x8 zx = join(lds_read_tr(zr), lds_read_tr(zr + 16 * F::XLD));
-      const uint16_t* br = &Bs[(4 * g + (lr >> 2)) * F::BLD + 4 * (lr & 3)];
+      const uint16_t* br = &Bs[(4 * g + (lr >> 2)) * F::BLD + 4 * (lr & 3) + 16 * hf * F::NABH];
 #pragma unroll
-      for (int ab = 0; ab < F::NAB; ++ab) {
-        const bf16x8 bt = join(lds_read_tr(br + 16 * ab), lds_read_tr(br + 16 * ab + 16 * F::BLD));
-        Sacc[ab] = mfma(bt, zx, Sacc[ab] * gL);
+      for (int l = 0; l < F::NABH; ++l) {
+        const bf16x8 bt = join(lds_read_tr(br + 16 * l), lds_read_tr(br + 16 * l + 16 * F::BLD));
+        Sacc[l] = mfma(bt, zx, Sacc[l] * gL);
       }
     }
     lds_barrier();  // every read of this chunk's tiles is done
@@ -256,9 +280,10 @@ __global__ __launch_bounds__(kThreads, DA >= 512 ? 1 : 2) void bwd_pass_mfma_ker
   if (p.s_out != nullptr) {
     const int x = c0 + cw + lr;
 #pragma unroll
-    for (int ab = 0; ab < F::NAB; ++ab)
+    for (int l = 0; l < F::NABH; ++l)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p.s_out[sb + static_cast<long>(16 * ab + 4 * g + i) * DX + x] = Sacc[ab][i];
+      for (int i = 0; i < 4; ++i)
+        p.s_out[sb + static_cast<long>(16 * (hf * F::NABH + l) + 4 * g + i) * DX + x] = Sacc[l][i];
   }
 }
 
@@ -266,7 +291,7 @@ template <int DA>
 void launch_da(const MPassSet& ps, int dx, int B, const HeadDecay& hd, int H, const HeadGroup& g, int T,
                hipStream_t s) {
   const dim3 grid(dx / kTX * B * g.nh * ps.npass);
-  hipLaunchKernelGGL(bwd_pass_mfma_kernel<DA>, grid, dim3(kThreads), 0, s, ps, hd, H, g.h0, g.nh, T);
+  hipLaunchKernelGGL(bwd_pass_mfma_kernel<DA>, grid, dim3(BCfg<DA>::NT), 0, s, ps, hd, H, g.h0, g.nh, T);
 }
 
 void launch_by_da(int da, const MPassSet& ps, int dx, int B, const HeadDecay& hd, int H, const HeadGroup& g, int T,
