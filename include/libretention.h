@@ -121,6 +121,11 @@ size_t retention_chunkwise_workspace_bytes(int B, int H, int T, int dk, int dv, 
  *   grad_q, grad_k : written, [B,H,T,dk] in dt.   grad_v : written, [B,H,T,dv] in dt.
  *   grad_state_in  : nullable; written, fp32 [B,H,dk,dv].  May be the
  *                    grad_state_out buffer exactly (in place).
+ *   workspace      : device scratch of at least retention_chunkwise_bwd_workspace_bytes()
+ *                    bytes (may be NULL when that is 0), owned by the caller,
+ *                    16-byte aligned, overlapping no other argument; contents
+ *                    on entry ignored, on return undefined.  A missing or
+ *                    short workspace is RET_ERR_INVALID_ARG.
  * The written gradients must not overlap each other or any input (apart from
  * that in-place case).  C is the chunk length of the forward call (validated
  * like there); the gradients do not depend on it beyond rounding, and the
@@ -131,7 +136,16 @@ size_t retention_chunkwise_workspace_bytes(int B, int H, int T, int dk, int dv, 
 ret_status retention_chunkwise_bwd(const void* q, const void* k, const void* v, const float* gamma,
                                    const float* state_in, const void* grad_y, const float* grad_state_out,
                                    void* grad_q, void* grad_k, void* grad_v, float* grad_state_in, int B, int H,
-                                   int T, int dk, int dv, int C, ret_dtype dt, void* stream);
+                                   int T, int dk, int dv, int C, ret_dtype dt, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* Workspace size for retention_chunkwise_bwd with these arguments (0 when the
+ * call needs none: fp32 inputs, or enough (batch, head, column) walkers to fill
+ * the device).  Few heads over a long sequence are split into sequence
+ * segments whose incoming states are found by a scan; the workspace holds one
+ * fp32 state per segment and pass: 3 * nseg * B*H*dk*dv * 4 bytes.  Returns
+ * (size_t)-1 for arguments the call would reject. */
+size_t retention_chunkwise_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C, ret_dtype dt);
 
 /*
  * Per-head GroupNorm of a retention output: every head is one group (the

@@ -30,7 +30,8 @@ SIGNATURES = {
     "retention_recurrent_step": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "retention_group_norm": (_i, [_vp, _vp, _vp, ctypes.c_float, _vp, _i, _i, _i, _i, _i, _vp]),
     "retention_chunkwise_bwd": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
-                                     _i, _vp]),
+                                     _i, _vp, _sz, _vp]),
+    "retention_chunkwise_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "retention_last_error": (ctypes.c_char_p, []),
     "retention_version": (_i, []),
 }
@@ -183,14 +184,16 @@ def chunkwise_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma, C: i
 
 def chunkwise_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma, C: int, grad_y: torch.Tensor,
                   state_in: Optional[torch.Tensor] = None, grad_state_out: Optional[torch.Tensor] = None,
-                  grad_state_in: Union[torch.Tensor, bool, None] = True
+                  grad_state_in: Union[torch.Tensor, bool, None] = True, workspace: Optional[torch.Tensor] = None
                   ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
     """Gradients of chunkwise_fwd on the GPU (retention_chunkwise_bwd).
 
     q, k, v, gamma, C, state_in: the forward call's arguments.  grad_y: [B,H,T,dv]
     in the input dtype; grad_state_out: optional fp32 [B,H,dk,dv].
     grad_state_in: a tensor to fill (may be grad_state_out), True to allocate
-    one, or False/None for none.  Returns (grad_q, grad_k, grad_v, grad_state_in).
+    one, or False/None for none.  workspace: device scratch (allocated here when
+    the call needs one and none is given).  Returns (grad_q, grad_k, grad_v,
+    grad_state_in).
     """
     lib = load()
     B, H, T, dk, dv, dt = _qkv(q, k, v)
@@ -208,9 +211,18 @@ def chunkwise_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma, C: i
     gq = torch.empty_like(q)
     gk = torch.empty_like(k)
     gv = torch.empty_like(v)
+    need = int(lib.retention_chunkwise_bwd_workspace_bytes(B, H, T, dk, dv, int(C), dt))
+    ws_bytes = 0
+    if need and need != ctypes.c_size_t(-1).value:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    elif workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
     st = lib.retention_chunkwise_bwd(_ptr(q), _ptr(k), _ptr(v), _gamma_array(gamma, H), _ptr(state_in),
                                      _ptr(grad_y), _ptr(grad_state_out), _ptr(gq), _ptr(gk), _ptr(gv),
-                                     _ptr(grad_state_in), B, H, T, dk, dv, int(C), dt, _stream(q.device))
+                                     _ptr(grad_state_in), B, H, T, dk, dv, int(C), dt, _ptr(workspace), ws_bytes,
+                                     _stream(q.device))
     _check(st)
     return gq, gk, gv, grad_state_in
 

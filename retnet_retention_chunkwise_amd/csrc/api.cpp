@@ -209,10 +209,19 @@ ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, 
   });
 }
 
+size_t retention_chunkwise_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C, ret_dtype dt) {
+  if (B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1 || C < 1) return static_cast<size_t>(-1);
+  if (dk > RET_MAX_DK || dv > RET_MAX_DV || C > RET_MAX_CHUNK) return static_cast<size_t>(-1);
+  if (dt != RET_F32 && dt != RET_BF16) return static_cast<size_t>(-1);
+  if (T == 0 || !ret::chunkwise_bwd_mfma_supports(dk, dv, static_cast<int>(dt))) return 0;
+  return ret::chunkwise_bwd_workspace_floats(B, H, T, dk, dv) * sizeof(float);
+}
+
 ret_status retention_chunkwise_bwd(const void* q, const void* k, const void* v, const float* gamma,
                                    const float* state_in, const void* grad_y, const float* grad_state_out,
                                    void* grad_q, void* grad_k, void* grad_v, float* grad_state_in, int B, int H,
-                                   int T, int dk, int dv, int C, ret_dtype dt, void* stream) {
+                                   int T, int dk, int dv, int C, ret_dtype dt, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
   const char* fn = "retention_chunkwise_bwd";
   ret_status st = check_common(fn, B, H, T, dk, dv, dt, gamma);
   if (st != RET_OK) return st;
@@ -222,7 +231,7 @@ ret_status retention_chunkwise_bwd(const void* q, const void* k, const void* v, 
     return fail(RET_ERR_INVALID_ARG, "%s: q, k, v, grad_y, grad_q, grad_k and grad_v are required", fn);
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(state_in) || misaligned(grad_y) ||
       misaligned(grad_state_out) || misaligned(grad_q) || misaligned(grad_k) || misaligned(grad_v) ||
-      misaligned(grad_state_in))
+      misaligned(grad_state_in) || misaligned(workspace))
     return fail(RET_ERR_UNSUPPORTED, "%s: tensor pointers must be 16-byte aligned", fn);
   if (!ret::chunkwise_bwd_generic_supports(dk, dv))
     return fail(RET_ERR_UNSUPPORTED, "%s: dk=%d, dv=%d not supported", fn, dk, dv);
@@ -234,8 +243,17 @@ ret_status retention_chunkwise_bwd(const void* q, const void* k, const void* v, 
     const void* p;
     size_t n;
   };
+  const size_t need = retention_chunkwise_bwd_workspace_bytes(B, H, T, dk, dv, C, dt);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(RET_ERR_INVALID_ARG, "%s: workspace of %zu bytes required, %zu given", fn, need, workspace_bytes);
   const Buf ins[] = {{q, nk}, {k, nk}, {v, nv}, {grad_y, nv}, {state_in, ns}, {grad_state_out, ns}};
   const Buf outs[] = {{grad_q, nk}, {grad_k, nk}, {grad_v, nv}, {grad_state_in, ns}};
+  if (need > 0) {
+    for (const Buf& b : ins)
+      if (overlap(workspace, need, b.p, b.n)) return fail(RET_ERR_INVALID_ARG, "%s: workspace overlaps another argument", fn);
+    for (const Buf& b : outs)
+      if (overlap(workspace, need, b.p, b.n)) return fail(RET_ERR_INVALID_ARG, "%s: workspace overlaps another argument", fn);
+  }
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j) {
       const bool in_place = i == 3 && j == 5 && outs[i].p == ins[j].p;
@@ -255,7 +273,7 @@ ret_status retention_chunkwise_bwd(const void* q, const void* k, const void* v, 
   const ret::BwdArgs a{q, k, v, state_in, grad_y, grad_state_out, grad_q, grad_k, grad_v, grad_state_in};
   const bool mfma = ret::chunkwise_bwd_mfma_supports(dk, dv, static_cast<int>(dt));
   return for_head_groups(fn, H, gamma, [&](const ret::HeadGroup& g) {
-    if (mfma) return ret::launch_chunkwise_bwd_mfma(a, B, H, T, dk, dv, g, s);
+    if (mfma) return ret::launch_chunkwise_bwd_mfma(a, B, H, T, dk, dv, static_cast<float*>(workspace), g, s);
     return ret::launch_chunkwise_bwd_generic(a, B, H, T, dk, dv, static_cast<int>(dt), g, s);
   });
 }

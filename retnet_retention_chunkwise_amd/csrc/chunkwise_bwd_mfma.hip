@@ -61,10 +61,19 @@ struct MPass {
   int s0_t;
   int rev;
   int dx;
+  float* ws;       // segmented calls: state slots, slot s at ws + s * ws_stride ([BH, DA, DX])
+  long ws_stride;
 };
+// Sequence segments (for few heads over long sequences): with nseg > 1 a pass
+// runs as a state-only launch over every segment but the first in its
+// direction (local end states from zero, into the slots), a scan over the
+// slots (incoming state of every segment), and the full launch per segment.
 struct MPassSet {
   MPass p[2];
-  int npass;  // passes of the launch (same d_a and d_x)
+  int npass;    // passes of the launch (same d_a and d_x)
+  int nseg;     // segments (1: none)
+  int seg_len;  // tokens per segment, a multiple of the chunk
+  int full;     // 1: outputs and final state; 0: state-only launch
 };
 
 template <int DA>
@@ -101,12 +110,19 @@ __global__ __launch_bounds__(BCfg<DA>::NT) void bwd_pass_mfma_kernel(MPassSet ps
   const int lin = blockIdx.x;
   const int item = (nwg % 8 == 0) ? (lin % 8) * (nwg / 8) + lin / 8 : lin;
   const int tiles = ps.p[0].dx / kTX;
+  const int nsl = ps.full ? ps.nseg : ps.nseg - 1;  // segment launches per (head, pass)
   const int tile = item % tiles;
-  const int pz = (item / tiles) % ps.npass;
-  const int hitem = item / (tiles * ps.npass);
+  const int segl = (item / tiles) % nsl;
+  const int pz = (item / (tiles * nsl)) % ps.npass;
+  const int hitem = item / (tiles * nsl * ps.npass);
   const MPass p = ps.p[pz];
   const int DX = p.dx;
   const bool rev = p.rev != 0;
+  const bool full = ps.full != 0;
+  // the state-only launch skips the segment processed first in the pass's direction
+  const int seg = (!full && rev) ? segl + 1 : segl;
+  const int t_begin = seg * ps.seg_len;
+  const int t_end = min(Tn, t_begin + ps.seg_len);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -127,6 +143,23 @@ __global__ __launch_bounds__(BCfg<DA>::NT) void bwd_pass_mfma_kernel(MPassSet ps
   const rsrc_t ro = make_rsrc(p.out + head * Tn * DX, static_cast<uint32_t>(Tn) * DX * 2);
   const long sb = head * static_cast<long>(DA) * DX;
 
+  // incoming state: the pass's S_0 (one segment), the scanned slot of this
+  // segment, or zero (state-only launch); outgoing: the pass's final state
+  // (the segment processed last) or, state-only, the next segment's slot
+  const float* init = nullptr;
+  bool init_t = false;
+  float* endp = nullptr;
+  if (ps.nseg == 1) {
+    init = p.s0;
+    init_t = p.s0_t != 0;
+    endp = p.s_out;
+  } else if (full) {
+    init = p.ws + seg * p.ws_stride;
+    if (seg == (rev ? 0 : ps.nseg - 1)) endp = p.s_out;
+  } else {
+    endp = p.ws + (rev ? seg - 1 : seg + 1) * p.ws_stride;
+  }
+
   // state: S[16 (hf NABH + l) + 4 g + i][c0 + cw + lr] in Sacc[l][i]
   f32x4 Sacc[F::NABH];
   {
@@ -135,12 +168,12 @@ __global__ __launch_bounds__(BCfg<DA>::NT) void bwd_pass_mfma_kernel(MPassSet ps
     for (int l = 0; l < F::NABH; ++l) {
       const int a = 16 * (hf * F::NABH + l) + 4 * g;
       f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (p.s0 != nullptr) {
-        if (p.s0_t) {
-          v = *reinterpret_cast<const f32x4*>(p.s0 + sb + static_cast<long>(x) * DA + a);
+      if (init != nullptr) {
+        if (init_t) {
+          v = *reinterpret_cast<const f32x4*>(init + sb + static_cast<long>(x) * DA + a);
         } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = p.s0[sb + static_cast<long>(a + i) * DX + x];
+          for (int i = 0; i < 4; ++i) v[i] = init[sb + static_cast<long>(a + i) * DX + x];
         }
       }
       Sacc[l] = v;
@@ -159,26 +192,26 @@ __global__ __launch_bounds__(BCfg<DA>::NT) void bwd_pass_mfma_kernel(MPassSet ps
       const int q = tid + F::NT * r;
       if (q < F::NP) {
         const uint32_t off = (static_cast<uint32_t>(t0 + q / PPR) * DA + (q % PPR) * 8) * 2;
-        pa[r] = buffer_load16(ra, off);
+        if (full) pa[r] = buffer_load16(ra, off);  // A feeds only the outputs
         pb[r] = buffer_load16(rb, off);
       }
     }
     if (xthr) px = buffer_load16(rx, (static_cast<uint32_t>(t0 + xj) * DX + c0 + xc) * 2);
   };
 
-  const int nch = (Tn + kCT - 1) / kCT;
+  const int nch = (t_end - t_begin + kCT - 1) / kCT;
   const float gL_full = gamma_pow(lg, kCT);
-  prefetch((rev ? nch - 1 : 0) * kCT);
+  prefetch(t_begin + (rev ? nch - 1 : 0) * kCT);
   for (int it = 0; it < nch; ++it) {
     const int ci = rev ? nch - 1 - it : it;
-    const int t0 = ci * kCT;
-    const int L = min(kCT, Tn - t0);
+    const int t0 = t_begin + ci * kCT;
+    const int L = min(kCT, t_end - t0);
     // ---- stage this chunk (the previous chunk ended with a barrier)
 #pragma unroll
     for (int r = 0; r < F::NLD; ++r) {
       const int q = tid + F::NT * r;
       if (q < F::NP) {
-        *reinterpret_cast<u32x4*>(&As[(q / PPR) * F::ALD + (q % PPR) * 8]) = pa[r];
+        if (full) *reinterpret_cast<u32x4*>(&As[(q / PPR) * F::ALD + (q % PPR) * 8]) = pa[r];
         *reinterpret_cast<u32x4*>(&Bs[(q / PPR) * F::BLD + (q % PPR) * 8]) = pb[r];
       }
     }
@@ -191,12 +224,12 @@ __global__ __launch_bounds__(BCfg<DA>::NT) void bwd_pass_mfma_kernel(MPassSet ps
       for (int e = 0; e < 8; ++e) zv[e] = static_cast<__bf16>(z * static_cast<float>(xv[e]));
       *reinterpret_cast<bf16x8*>(&Zs[xj * F::XLD + xc]) = zv;
     }
-    if (it + 1 < nch) prefetch((rev ? ci - 1 : ci + 1) * kCT);
+    if (it + 1 < nch) prefetch(t_begin + (rev ? ci - 1 : ci + 1) * kCT);
     lds_barrier();
 
     // ---- scores (waves of the upper half): tile (jb, jpb) = strip cs, masked
     // and decayed, to LDS in bf16
-    if (hf == 1) {
+    if (full && hf == 1) {
       const int jb = cs >> 1, jpb = cs & 1;
       const bool live = rev ? jpb >= jb : jpb <= jb;
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -224,23 +257,25 @@ __global__ __launch_bounds__(BCfg<DA>::NT) void bwd_pass_mfma_kernel(MPassSet ps
     for (int jb = 0; jb < 2; ++jb) O[jb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int sl = 0; sl < F::NSH; ++sl) {
-      const int s = hf * F::NSH + sl;
-      const bf16x8 sv = pack_bf16x8(Sacc[2 * sl], Sacc[2 * sl + 1]);
+      if (full) {
+        const int s = hf * F::NSH + sl;
+        const bf16x8 sv = pack_bf16x8(Sacc[2 * sl], Sacc[2 * sl + 1]);
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        const uint16_t* row = &As[(16 * jb + lr) * F::ALD + 32 * s + 4 * g];
-        const bf16x8 av = join(*reinterpret_cast<const s16x4*>(row), *reinterpret_cast<const s16x4*>(row + 16));
-        O[jb] = mfma(sv, av, O[jb]);
+        for (int jb = 0; jb < 2; ++jb) {
+          const uint16_t* row = &As[(16 * jb + lr) * F::ALD + 32 * s + 4 * g];
+          const bf16x8 av = join(*reinterpret_cast<const s16x4*>(row), *reinterpret_cast<const s16x4*>(row + 16));
+          O[jb] = mfma(sv, av, O[jb]);
+        }
       }
     }
-    if (hf >= 1) {
+    if (full && hf >= 1) {
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) Xch[hf - 1][cs][jb][lane] = O[jb];
     }
     lds_barrier();  // scores and upper partials are in LDS
 
     // ---- outputs (lower half): add the partner's partial, scale, + X^T P^T
-    if (hf == 0) {
+    if (full && hf == 0) {
       const uint16_t* xr = &Xs[(4 * g + (lr >> 2)) * F::XLD + cw + 4 * (lr & 3)];
       const bf16x8 xt = join(lds_read_tr(xr), lds_read_tr(xr + 16 * F::XLD));
 #pragma unroll
@@ -277,30 +312,87 @@ __global__ __launch_bounds__(BCfg<DA>::NT) void bwd_pass_mfma_kernel(MPassSet ps
     lds_barrier();  // every read of this chunk's tiles is done
   }
 
-  if (p.s_out != nullptr) {
+  if (endp != nullptr) {
     const int x = c0 + cw + lr;
 #pragma unroll
     for (int l = 0; l < F::NABH; ++l)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        p.s_out[sb + static_cast<long>(16 * (hf * F::NABH + l) + 4 * g + i) * DX + x] = Sacc[l][i];
+        endp[sb + static_cast<long>(16 * (hf * F::NABH + l) + 4 * g + i) * DX + x] = Sacc[l][i];
+  }
+}
+
+// Incoming state of every segment of one pass, in place over its slots
+// (slot s holds the local end state the state-only launch wrote):
+//   forward: slot 0 = S_0, slot s = gamma^seg_len slot(s-1) + slot s;
+//   reverse: slot nseg-1 = S_0, slot s = gamma^len(s+1) slot(s+1) + slot s.
+// S_0 is read in the pass's layout (transposed for s0_t).
+__global__ __launch_bounds__(256) void bwd_segment_scan_kernel(MPass p, int DA, HeadDecay gam, int H, int h0, int nh,
+                                                               int B, int Tn, int nseg, int seg_len) {
+  const long per_head = static_cast<long>(DA) * p.dx;
+  const long n = static_cast<long>(B) * nh * per_head;
+  for (long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x; idx < n;
+       idx += static_cast<long>(gridDim.x) * blockDim.x) {
+    const long bh = idx / per_head;
+    const long within = idx % per_head;
+    const int hl = static_cast<int>(bh % nh);
+    const long head = (bh / nh) * H + h0 + hl;
+    const long off = head * per_head + within;
+    const float lg = gam.log2g[hl];
+    float s = 0.0f;
+    if (p.s0 != nullptr) {
+      const long a = within / p.dx, x = within % p.dx;
+      s = p.s0_t ? p.s0[head * per_head + x * DA + a] : p.s0[off];
+    }
+    if (p.rev) {
+      p.ws[(nseg - 1) * p.ws_stride + off] = s;
+      for (int sg = nseg - 2; sg >= 0; --sg) {
+        const int len = min(seg_len, Tn - (sg + 1) * seg_len);
+        s = fmaf(gamma_pow(lg, len), s, p.ws[sg * p.ws_stride + off]);
+        p.ws[sg * p.ws_stride + off] = s;
+      }
+    } else {
+      const float gs = gamma_pow(lg, seg_len);
+      p.ws[off] = s;
+      for (int sg = 1; sg < nseg; ++sg) {
+        s = fmaf(gs, s, p.ws[sg * p.ws_stride + off]);
+        p.ws[sg * p.ws_stride + off] = s;
+      }
+    }
   }
 }
 
 template <int DA>
-void launch_da(const MPassSet& ps, int dx, int B, const HeadDecay& hd, int H, const HeadGroup& g, int T,
-               hipStream_t s) {
-  const dim3 grid(dx / kTX * B * g.nh * ps.npass);
-  hipLaunchKernelGGL(bwd_pass_mfma_kernel<DA>, grid, dim3(BCfg<DA>::NT), 0, s, ps, hd, H, g.h0, g.nh, T);
+hipError_t launch_da(MPassSet ps, int B, const HeadDecay& hd, int H, const HeadGroup& g, int T, hipStream_t s) {
+  const int items = B * g.nh * ps.npass * (ps.p[0].dx / kTX);
+  if (ps.nseg > 1) {
+    ps.full = 0;
+    hipLaunchKernelGGL(bwd_pass_mfma_kernel<DA>, dim3(items * (ps.nseg - 1)), dim3(BCfg<DA>::NT), 0, s, ps, hd, H,
+                       g.h0, g.nh, T);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    for (int i = 0; i < ps.npass; ++i) {
+      const long n = static_cast<long>(B) * g.nh * DA * ps.p[i].dx;
+      const unsigned blocks = static_cast<unsigned>(min(65536L, (n + 255) / 256));
+      hipLaunchKernelGGL(bwd_segment_scan_kernel, dim3(blocks), dim3(256), 0, s, ps.p[i], DA, hd, H, g.h0, g.nh, B,
+                         T, ps.nseg, ps.seg_len);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  ps.full = 1;
+  hipLaunchKernelGGL(bwd_pass_mfma_kernel<DA>, dim3(items * ps.nseg), dim3(BCfg<DA>::NT), 0, s, ps, hd, H, g.h0,
+                     g.nh, T);
+  return hipGetLastError();
 }
 
-void launch_by_da(int da, const MPassSet& ps, int dx, int B, const HeadDecay& hd, int H, const HeadGroup& g, int T,
-                  hipStream_t s) {
+hipError_t launch_by_da(int da, const MPassSet& ps, int B, const HeadDecay& hd, int H, const HeadGroup& g, int T,
+                        hipStream_t s) {
   switch (da) {
-    case 64: launch_da<64>(ps, dx, B, hd, H, g, T, s); break;
-    case 128: launch_da<128>(ps, dx, B, hd, H, g, T, s); break;
-    case 256: launch_da<256>(ps, dx, B, hd, H, g, T, s); break;
-    default: launch_da<512>(ps, dx, B, hd, H, g, T, s); break;
+    case 64: return launch_da<64>(ps, B, hd, H, g, T, s);
+    case 128: return launch_da<128>(ps, B, hd, H, g, T, s);
+    case 256: return launch_da<256>(ps, B, hd, H, g, T, s);
+    default: return launch_da<512>(ps, B, hd, H, g, T, s);
   }
 }
 
@@ -310,27 +402,61 @@ bool da_ok(int d) { return d == 64 || d == 128 || d == 256 || d == 512; }
 
 bool chunkwise_bwd_mfma_supports(int dk, int dv, int dt) { return dt == 1 && da_ok(dk) && da_ok(dv); }
 
-hipError_t launch_chunkwise_bwd_mfma(const BwdArgs& a, int B, int H, int T, int dk, int dv, const HeadGroup& g,
-                                     hipStream_t s) {
+// Few (batch, head, column tile) walkers over a long sequence: split into
+// segments of at least kMinSegChunks chunks so that the smaller of the two
+// launches fills about kTargetWorkgroups workgroups.  A pure function of the
+// sizes.
+ChunkSegments chunkwise_bwd_segments(int B, int H, int T, int dk, int dv) {
+  constexpr long kTargetWorkgroups = 256;  // MI355X compute units
+  constexpr int kMinSegChunks = 8;
+  ChunkSegments r{T > 0 ? T : 1, 1};
+  const long walkers = static_cast<long>(B) * H * min(2 * (dk / kTX), dv / kTX);
+  const long nchunks = (static_cast<long>(T) + kCT - 1) / kCT;
+  if (walkers < 1 || walkers >= kTargetWorkgroups || nchunks < 2 * kMinSegChunks) return r;
+  long want = (kTargetWorkgroups + walkers - 1) / walkers;
+  want = min(want, nchunks / kMinSegChunks);
+  if (want < 2) return r;
+  const long per = (nchunks + want - 1) / want;  // chunks per segment
+  r.seg_len = static_cast<int>(per * kCT);
+  r.nseg = static_cast<int>((nchunks + per - 1) / per);
+  return r;
+}
+
+size_t chunkwise_bwd_workspace_floats(int B, int H, int T, int dk, int dv) {
+  const ChunkSegments sg = chunkwise_bwd_segments(B, H, T, dk, dv);
+  if (sg.nseg <= 1) return 0;
+  return static_cast<size_t>(3) * sg.nseg * B * H * dk * dv;  // dV, dK and dQ passes
+}
+
+hipError_t launch_chunkwise_bwd_mfma(const BwdArgs& a, int B, int H, int T, int dk, int dv, float* ws,
+                                     const HeadGroup& g, hipStream_t s) {
   const HeadDecay hd = make_head_decay(g);
   auto u = [](const void* x) { return static_cast<const uint16_t*>(x); };
+  const ChunkSegments sg = chunkwise_bwd_segments(B, H, T, dk, dv);
+  const long stride = static_cast<long>(B) * H * dk * dv;  // one slot
+  float* wv = sg.nseg > 1 ? ws : nullptr;
+  float* wk = sg.nseg > 1 ? ws + sg.nseg * stride : nullptr;
+  float* wq = sg.nseg > 1 ? ws + 2 * sg.nseg * stride : nullptr;
   // dK (reverse over V, dY, Q from dS_out^T) and dQ (forward over dY, V, K from
   // S_in^T) share d_a = dv: one launch
   MPassSet kq{};
-  kq.p[0] = MPass{u(a.v), u(a.dy), u(a.q), static_cast<uint16_t*>(a.dk), a.dstate_out, nullptr, 1, 1, dk};
-  kq.p[1] = MPass{u(a.dy), u(a.v), u(a.k), static_cast<uint16_t*>(a.dq), a.state_in, nullptr, 1, 0, dk};
+  kq.p[0] = MPass{u(a.v), u(a.dy), u(a.q), static_cast<uint16_t*>(a.dk), a.dstate_out, nullptr, 1, 1, dk, wk, stride};
+  kq.p[1] = MPass{u(a.dy), u(a.v), u(a.k), static_cast<uint16_t*>(a.dq), a.state_in, nullptr, 1, 0, dk, wq, stride};
   kq.npass = 2;
-  launch_by_da(dv, kq, dk, B, hd, H, g, T, s);
-  hipError_t e = hipGetLastError();
+  kq.nseg = sg.nseg;
+  kq.seg_len = sg.seg_len;
+  hipError_t e = launch_by_da(dv, kq, B, hd, H, g, T, s);
   if (e != hipSuccess) return e;
   // dV (reverse over K, Q, dY from dS_out); final state = dS_in.  After the dK
   // pass, so that dstate_in may be the dstate_out buffer.
   MPassSet vs{};
-  vs.p[0] = MPass{u(a.k), u(a.q), u(a.dy), static_cast<uint16_t*>(a.dv), a.dstate_out, a.dstate_in, 0, 1, dv};
+  vs.p[0] = MPass{u(a.k), u(a.q), u(a.dy), static_cast<uint16_t*>(a.dv), a.dstate_out, a.dstate_in, 0, 1, dv, wv,
+                  stride};
   vs.p[1] = vs.p[0];
   vs.npass = 1;
-  launch_by_da(dk, vs, dv, B, hd, H, g, T, s);
-  return hipGetLastError();
+  vs.nseg = sg.nseg;
+  vs.seg_len = sg.seg_len;
+  return launch_by_da(dk, vs, B, hd, H, g, T, s);
 }
 
 }  // namespace ret

@@ -76,8 +76,13 @@ hipError_t launch_chunkwise_bwd_generic(const BwdArgs& a, int B, int H, int T, i
                                         const HeadGroup& g, hipStream_t s);
 // bf16 MFMA passes: bf16 inputs with dk, dv in {64, 128, 256, 512}.
 bool chunkwise_bwd_mfma_supports(int dk, int dv, int dt);
-hipError_t launch_chunkwise_bwd_mfma(const BwdArgs& a, int B, int H, int T, int dk, int dv, const HeadGroup& g,
-                                     hipStream_t s);
+// Sequence segments of a backward call on the MFMA passes, and the fp32
+// workspace they need (0: none); pure functions of the sizes.
+ChunkSegments chunkwise_bwd_segments(int B, int H, int T, int dk, int dv);
+size_t chunkwise_bwd_workspace_floats(int B, int H, int T, int dk, int dv);
+// ws: chunkwise_bwd_workspace_floats(...) fp32 (unused when 0)
+hipError_t launch_chunkwise_bwd_mfma(const BwdArgs& a, int B, int H, int T, int dk, int dv, float* ws,
+                                     const HeadGroup& g, hipStream_t s);
 
 // Per-head GroupNorm of a [B,H,T,dv] output (dt: 0 = fp32, 1 = bf16); out may be y.
 hipError_t launch_group_norm(const void* y, const float* weight, const float* bias, float eps, void* out, int B,

@@ -175,7 +175,7 @@ def bwd(lib, q=FAKE, k=ctypes.c_void_p(0x100000), v=ctypes.c_void_p(0x200000), s
         dy=ctypes.c_void_p(0x300000), dso=None, gq=ctypes.c_void_p(0x400000), gk=ctypes.c_void_p(0x500000),
         gv=ctypes.c_void_p(0x600000), gsi=None, B=1, H=2, T=8, dk=16, dv=16, C=4, dt=0):
     return lib.retention_chunkwise_bwd(q, k, v, gam(0.5, 0.9), sin, dy, dso, gq, gk, gv, gsi, B, H, T, dk, dv, C, dt,
-                                       None)
+                                       None, 0, None)
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -215,9 +215,11 @@ def test_host_dispatch_of_every_backward_parity_shape_without_a_device(lib):
     import test_parity_gpu as parity
     for (B, H, T, dk, dv, C, dt, _, _, _) in parity.BWD_CASES:
         d = 1 if dt == "bf16" else 0
-        ptrs = [ctypes.c_void_p(a << 36) for a in range(1, 8)]
+        ptrs = [ctypes.c_void_p(a << 36) for a in range(1, 9)]
+        need = lib.retention_chunkwise_bwd_workspace_bytes(B, H, T, dk, dv, C, d)
         st = lib.retention_chunkwise_bwd(ptrs[0], ptrs[1], ptrs[2], gam(*([0.5] * H)), None, ptrs[3], None,
-                                         ptrs[4], ptrs[5], ptrs[6], None, B, H, T, dk, dv, C, d, None)
+                                         ptrs[4], ptrs[5], ptrs[6], None, B, H, T, dk, dv, C, d,
+                                         ptrs[7] if need else None, need, None)
         assert st == 3, (B, H, T, dk, dv, C, dt, _lib.last_error())
 
 
@@ -266,3 +268,29 @@ def test_host_dispatch_of_every_group_norm_parity_shape_without_a_device(lib):
         w = ctypes.c_void_p(3 << 36) if affine else None
         b = ctypes.c_void_p(4 << 36) if affine else None
         assert lib.retention_group_norm(y, w, b, eps, out, B, H, T, dv, d, None) == 3, _lib.last_error()
+
+
+def test_backward_workspace_for_segmented_long_sequences(lib):
+    """bf16 backward calls with few (batch, head, column) walkers over a long
+    sequence are split into sequence segments: one fp32 state slot per segment
+    and pass (dV, dK, dQ)."""
+    # B1 H8 T65536 dk256 dv512: 64 walkers -> 4 segments
+    assert lib.retention_chunkwise_bwd_workspace_bytes(1, 8, 65536, 256, 512, 128, 1) == 3 * 4 * 8 * 256 * 512 * 4
+    # the 1.3B layer (B4 H8 T2048): 256 walkers, no segments
+    assert lib.retention_chunkwise_bwd_workspace_bytes(4, 8, 2048, 256, 512, 64, 1) == 0
+    # fp32 inputs (generic passes) and short sequences never segment
+    assert lib.retention_chunkwise_bwd_workspace_bytes(1, 1, 65536, 64, 64, 64, 0) == 0
+    assert lib.retention_chunkwise_bwd_workspace_bytes(1, 1, 15 * 32, 64, 64, 64, 1) == 0
+    bad = ctypes.c_size_t(-1).value
+    assert lib.retention_chunkwise_bwd_workspace_bytes(1, 1, 64, 64, 64, 0, 1) == bad
+
+
+def test_segmented_backward_requires_workspace(lib):
+    q, k, v, dy, gq, gk, gv = (ctypes.c_void_p(a << 36) for a in range(1, 8))
+    need = lib.retention_chunkwise_bwd_workspace_bytes(1, 2, 4096, 64, 64, 64, 1)
+    assert need > 0
+    args = dict(q=q, k=k, v=v, dy=dy, gq=gq, gk=gk, gv=gv, B=1, H=2, T=4096, dk=64, dv=64, C=64, dt=1)
+    assert bwd(lib, **args) == INVALID and "workspace" in _lib.last_error()
+    st = lib.retention_chunkwise_bwd(q, k, v, gam(0.5, 0.9), None, dy, None, gq, gk, gv, None, 1, 2, 4096, 64, 64, 64,
+                                     1, ctypes.c_void_p((1 << 36) + 4096), need, None)
+    assert st == INVALID and "workspace overlaps" in _lib.last_error()

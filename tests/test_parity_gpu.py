@@ -171,6 +171,12 @@ BWD_CASES = [
     (2, 2, 257, 256, 512, 128, "bf16", False, False, [0.999, 0.8]),
     (1, 2, 1, 256, 256, 1, "bf16", True, True, [0.9, 0.6]),
     (1, 130, 40, 64, 64, 32, "bf16", True, True, None),
+    # few walkers over long sequences: sequence segments (state-only launch,
+    # scan over segments in each pass's direction, full launch), incl. a short
+    # last segment and gamma = 1
+    (1, 1, 4096, 64, 64, 64, "bf16", True, True, [0.999]),
+    (1, 2, 3001, 128, 256, 64, "bf16", True, True, [0.995, 0.9]),
+    (1, 1, 2500, 256, 512, 128, "bf16", False, False, [1.0]),
 ]
 
 
@@ -215,6 +221,24 @@ def test_chunkwise_bwd_sampled_heads_at_layer_size(dt):
         ref = oracle.recurrent_backward(sl(q), sl(k), sl(v), torch.tensor([gs[h]]), sl(dy), sl(s0), sl(ds))
         for name, gg, r in zip(("grad_q", "grad_k", "grad_v", "grad_state_in"), got, ref):
             check(f"{name} (b{b} h{h})", sl(gg), r, tol(q.dtype))
+
+
+def test_segmented_bwd_in_place_and_explicit_workspace():
+    """A segmented bf16 backward with grad_state_in = grad_state_out (in place)
+    and a caller-provided workspace."""
+    B, H, T, dk, dv = 1, 2, 2048, 64, 128
+    gs = [0.99, 0.7]
+    say("segmented backward, in place, explicit workspace")
+    q, k, v, s0, dy, ds = bwd_inputs(B, H, T, dk, dv, "bf16", seed=43)
+    ref = oracle.recurrent_backward(q, k, v, torch.tensor(gs), dy, s0, ds)
+    qd, kd, vd, sd, dyd, dsd = to_dev(q, k, v, s0, dy, ds)
+    need = int(ret.load().retention_chunkwise_bwd_workspace_bytes(B, H, T, dk, dv, 64, 1))
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    got = ret.chunkwise_bwd(qd, kd, vd, gs, 64, dyd, state_in=sd, grad_state_out=dsd, grad_state_in=dsd, workspace=ws)
+    torch.cuda.synchronize()
+    for name, g, r in zip(("grad_q", "grad_k", "grad_v", "grad_state_in"), got, ref):
+        check(name, g, r, 2e-2)
 
 
 def test_chunkwise_bwd_in_place_state_gradient_and_empty_sequence():
