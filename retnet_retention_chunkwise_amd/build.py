@@ -32,6 +32,7 @@ SOURCES = [
     "chunkwise_bwd.hip",
     "chunkwise_bwd_mfma.hip",
     "group_norm.hip",
+    "chunkwise_f32_mfma.hip",
 ]
 
 ARCH = "gfx950"

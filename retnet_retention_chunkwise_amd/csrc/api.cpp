@@ -200,10 +200,15 @@ ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, 
     });
   }
   const bool mfma = ret::chunkwise_mfma_supports(T, dk, dv, C, static_cast<int>(dt));
+  const bool f32 = ret::chunkwise_f32_mfma_supports(dk, dv, static_cast<int>(dt));
   const ret::ChunkSegments segs = mfma ? ret::chunkwise_mfma_segments(B, H, T, dv, C) : ret::ChunkSegments{T, 1};
   float* ws = static_cast<float*>(workspace);
   return for_head_groups(fn, H, gamma, [&](const ret::HeadGroup& g) {
     if (mfma) return ret::launch_chunkwise_mfma(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, segs, ws, g, s);
+    if (f32)
+      return ret::launch_chunkwise_f32_fwd(static_cast<const float*>(q), static_cast<const float*>(k),
+                                           static_cast<const float*>(v), state_in, state_out, static_cast<float*>(y),
+                                           B, H, T, dk, dv, g, s);
     return ret::launch_chunkwise_generic(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, static_cast<int>(dt),
                                          g, s);
   });
@@ -272,8 +277,10 @@ ret_status retention_chunkwise_bwd(const void* q, const void* k, const void* v, 
   }
   const ret::BwdArgs a{q, k, v, state_in, grad_y, grad_state_out, grad_q, grad_k, grad_v, grad_state_in};
   const bool mfma = ret::chunkwise_bwd_mfma_supports(dk, dv, static_cast<int>(dt));
+  const bool f32 = ret::chunkwise_f32_mfma_supports(dk, dv, static_cast<int>(dt));
   return for_head_groups(fn, H, gamma, [&](const ret::HeadGroup& g) {
     if (mfma) return ret::launch_chunkwise_bwd_mfma(a, B, H, T, dk, dv, static_cast<float*>(workspace), g, s);
+    if (f32) return ret::launch_chunkwise_f32_bwd(a, B, H, T, dk, dv, g, s);
     return ret::launch_chunkwise_bwd_generic(a, B, H, T, dk, dv, static_cast<int>(dt), g, s);
   });
 }

@@ -59,6 +59,9 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void buffer_store8(rsrc_t r, uint32_t off, u32x2 x) {
   __builtin_amdgcn_raw_buffer_store_b64(x, r, static_cast<int>(off), 0, 0);
 }
+__device__ __forceinline__ void buffer_store16(rsrc_t r, uint32_t off, u32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, static_cast<int>(off), 0, 0);
+}
 
 // Eight fp32 values as an MFMA bf16 operand (round to nearest even).
 __device__ __forceinline__ bf16x8 pack_bf16x8(f32x4 lo, f32x4 hi) {

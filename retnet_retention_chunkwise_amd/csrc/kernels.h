@@ -84,6 +84,15 @@ size_t chunkwise_bwd_workspace_floats(int B, int H, int T, int dk, int dv);
 hipError_t launch_chunkwise_bwd_mfma(const BwdArgs& a, int B, int H, int T, int dk, int dv, float* ws,
                                      const HeadGroup& g, hipStream_t s);
 
+// fp32 inputs on fp32 MFMA (dk, dv in {64, 128, 256, 512}): the forward and
+// the backward passes of the chunkwise form at fp32 accuracy.
+bool chunkwise_f32_mfma_supports(int dk, int dv, int dt);
+hipError_t launch_chunkwise_f32_fwd(const float* q, const float* k, const float* v, const float* state_in,
+                                    float* state_out, float* y, int B, int H, int T, int dk, int dv,
+                                    const HeadGroup& g, hipStream_t s);
+hipError_t launch_chunkwise_f32_bwd(const BwdArgs& a, int B, int H, int T, int dk, int dv, const HeadGroup& g,
+                                    hipStream_t s);
+
 // Per-head GroupNorm of a [B,H,T,dv] output (dt: 0 = fp32, 1 = bf16); out may be y.
 hipError_t launch_group_norm(const void* y, const float* weight, const float* bias, float eps, void* out, int B,
                              int H, int T, int dv, int dt, hipStream_t s);

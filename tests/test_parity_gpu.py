@@ -65,6 +65,11 @@ CHUNK_CASES = [
     (1, 2, 300, 16, 16, 1, "f32", False, [0.8, 0.3]),
     (1, 2, 300, 32, 48, 128, "f32", True, [0.999, 0.5]),
     (1, 130, 20, 4, 4, 4, "f32", True, None),
+    # fp32 inputs on fp32 MFMA (dk, dv in {64..512}): every d_a instance, ragged tails
+    (2, 2, 257, 64, 64, 32, "f32", True, [0.9, 0.99]),
+    (1, 3, 100, 64, 128, 16, "f32", True, [0.0, 0.5, 1.0]),
+    (1, 2, 300, 128, 256, 64, "f32", False, [0.995, 0.8]),
+    (1, 2, 201, 256, 512, 128, "f32", True, [0.97, 0.999]),
     (1, 2, 300, 64, 128, 64, "bf16", True, [0.97, 0.6]),
     (2, 2, 200, 48, 80, 32, "bf16", False, [0.0, 1.0]),
     (1, 2, 129, 256, 512, 128, "bf16", True, [0.99, 0.9]),
@@ -161,6 +166,9 @@ BWD_CASES = [
     (1, 1, 1, 8, 8, 1, "f32", True, True, [0.7]),
     (1, 130, 20, 4, 4, 4, "f32", True, True, None),
     (2, 2, 70, 256, 512, 64, "f32", True, True, [0.97, 0.999]),
+    (1, 3, 100, 64, 64, 16, "f32", True, False, [0.0, 0.6, 1.0]),
+    (2, 2, 129, 128, 256, 64, "f32", False, True, [0.99, 0.9]),
+    (1, 130, 33, 64, 64, 32, "f32", True, True, None),
     (1, 2, 129, 128, 256, 64, "bf16", True, True, [0.99, 0.9]),
     (1, 2, 200, 256, 512, 64, "bf16", True, True, [0.97, 0.999]),
     (2, 2, 77, 48, 80, 32, "bf16", False, False, [0.0, 1.0]),
@@ -500,6 +508,22 @@ def test_chunkwise_in_a_captured_graph_matches_eager():
 # ------------------------------------------------------- full-size workloads
 def sampled_heads(B, H):
     return sorted({(0, 0), (B // 2, H // 2), (B - 1, H - 1)})
+
+
+def test_f32_forward_at_layer_size_sampled_heads():
+    """fp32 inputs at the 1.3B-scale layer shape (fp32 MFMA path): sampled
+    heads against the oracle at the fp32 bound."""
+    wl = WORKLOADS["layer1p3b"]
+    say("fp32 forward at layer size")
+    q, k, v, s0 = make_inputs(wl.B, wl.H, wl.T, wl.dk, wl.dv, "f32", seed=44, with_state=True)
+    qd, kd, vd, sd = to_dev(q, k, v, s0)
+    y, s = ret.chunkwise_fwd(qd, kd, vd, list(wl.gammas), wl.C, state_in=sd)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (3, 7)):
+        sl = lambda t: t[b:b + 1, h:h + 1]
+        y_ref, s_ref = oracle.recurrent(sl(q), sl(k), sl(v), torch.tensor([wl.gammas[h]]), sl(s0))
+        check(f"y (b{b} h{h})", sl(y), y_ref, 1e-4)
+        check(f"state (b{b} h{h})", sl(s), s_ref, 1e-4)
 
 
 @pytest.mark.parametrize("key", ["layer1p3b", "layer6p7b", "long64k"])
