@@ -90,6 +90,12 @@ ret_status retention_parallel_fwd(const void* q, const void* k, const void* v, c
  *               its contents on entry are ignored and on return undefined.  A
  *               missing or short workspace is RET_ERR_INVALID_ARG.
  * T = 0 is valid: y is untouched and state_out receives state_in (or zeros).
+ * The result does not depend on C beyond rounding.  Kernels: bf16 inputs with
+ * dk in {64,128,256} and dv % 64 == 0 run on bf16 MFMA with chunks of C; fp32
+ * inputs with dk, dv in {64,128,256,512} run on fp32 MFMA with 16-token
+ * chunks; blocks of T <= 16 tokens run as one chunk in a single streaming pass
+ * over the state; every other case runs on fp32 VALU arithmetic with chunks of
+ * C.  State and accumulators are fp32 throughout.
  */
 ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, const float* gamma,
                                    const float* state_in, float* state_out, void* y, int B, int H, int T,
@@ -131,7 +137,8 @@ size_t retention_chunkwise_workspace_bytes(int B, int H, int T, int dk, int dv, 
  * like there); the gradients do not depend on it beyond rounding, and the
  * kernels choose their own chunking.  State and accumulators are fp32; bf16
  * inputs with dk in {64, 128, 256} and dv in {64, 128, 256, 512} take bf16
- * MFMA products (as the forward does), every other case fp32 arithmetic.
+ * MFMA products (as the forward does), fp32 inputs with those dk and dv (and
+ * dk = 512) fp32 MFMA products, every other case fp32 VALU arithmetic.
  */
 ret_status retention_chunkwise_bwd(const void* q, const void* k, const void* v, const float* gamma,
                                    const float* state_in, const void* grad_y, const float* grad_state_out,
