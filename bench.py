@@ -12,7 +12,7 @@ reads cold data (one set, 201 MB, would fit in the 256 MB last-level cache).
 The recurrent decode step (retention_recurrent_step, batch 128, H=16, fp32
 256x512 state per head, 1000 chained steps) is measured in the same run and
 reported in the "decode" object, and a chunkwise continuation of 16 new tokens
-per stream from that state (the short-block streaming kernel) in the
+per stream from that state (the fp32-MFMA streaming kernel) in the
 "continuation" object, the backward of the chunkwise workload in "backward"
 and the per-head GroupNorm of its output in "group_norm".
 
@@ -243,7 +243,7 @@ def main():
 
     # ------------------------------------- multi-token continuation (16 tokens)
     # chunkwise on 16 new tokens per stream from the decode state, in place
-    # (the short-block streaming kernel)
+    # (the fp32-MFMA short-block streaming kernel)
     ct = 16
     cq, ck, cv = make_inputs(dw.B, dw.H, ct, dw.dk, dw.dv, dw.dtype, seed=1)
     cq, ck, cv = cq.to(dev), ck.to(dev), cv.to(dev)
@@ -261,8 +261,8 @@ def main():
     cont_us = statistics.median(a.elapsed_time(b) for a, b in cev) * 1e3
     cont_bytes = 2 * state_bytes + dw.B * dw.H * ct * (2 * dw.dk + 2 * dw.dk + 2 * dw.dv + 2 * dw.dv)
     cont_gbs = cont_bytes / (cont_us * 1e-6) / 1e9
-    cont_src = os.path.join(ROOT, "retnet_retention_chunkwise_amd", "csrc", "short_chunk.hip")
-    cont_traffic = load_traffic("short_chunk_continuation16_traffic.txt", cont_src)
+    cont_src = os.path.join(ROOT, "retnet_retention_chunkwise_amd", "csrc", "short_mfma.hip")
+    cont_traffic = load_traffic("short_mfma_continuation16_traffic.txt", cont_src)
     del cq, ck, cv, cstate, cy, s0
     torch.cuda.empty_cache()
 

@@ -33,6 +33,7 @@ SOURCES = [
     "chunkwise_bwd_mfma.hip",
     "group_norm.hip",
     "chunkwise_f32_mfma.hip",
+    "short_mfma.hip",
 ]
 
 ARCH = "gfx950"

@@ -144,6 +144,7 @@ size_t retention_chunkwise_workspace_bytes(int B, int H, int T, int dk, int dv, 
   if (dk > RET_MAX_DK || dv > RET_MAX_DV || C > RET_MAX_CHUNK) return static_cast<size_t>(-1);
   if (dt != RET_F32 && dt != RET_BF16) return static_cast<size_t>(-1);
   if (T <= ret::kShortChunkMaxT || !ret::chunkwise_mfma_supports(T, dk, dv, C, static_cast<int>(dt))) return 0;
+  if (T <= ret::kShortMfmaMaxT && T >= ret::kShortMfmaMinT && ret::short_mfma_supports(T, dk, dv)) return 0;
   const ret::ChunkSegments segs = ret::chunkwise_mfma_segments(B, H, T, dv, C);
   if (segs.nseg <= 1) return 0;
   return static_cast<size_t>(segs.nseg) * B * H * dk * dv * sizeof(float);
@@ -191,6 +192,12 @@ ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, 
     // one token continued in place: exactly the recurrent step
     return for_head_groups(fn, H, gamma, [&](const ret::HeadGroup& g) {
       return ret::launch_recurrent_step(q, k, v, state_out, y, B, H, dk, dv, static_cast<int>(dt), g, s);
+    });
+  }
+  if (T >= ret::kShortMfmaMinT && ret::short_mfma_supports(T, dk, dv)) {
+    // one chunk of T tokens on fp32 MFMA (the same result as any C up to rounding order)
+    return for_head_groups(fn, H, gamma, [&](const ret::HeadGroup& g) {
+      return ret::launch_short_mfma(q, k, v, state_in, state_out, y, B, H, T, dk, dv, static_cast<int>(dt), g, s);
     });
   }
   if (T <= ret::kShortChunkMaxT) {

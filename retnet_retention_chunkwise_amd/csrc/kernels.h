@@ -97,6 +97,13 @@ hipError_t launch_chunkwise_f32_bwd(const BwdArgs& a, int B, int H, int T, int d
 hipError_t launch_group_norm(const void* y, const float* weight, const float* bias, float eps, void* out, int B,
                              int H, int T, int dv, int dt, hipStream_t s);
 
+// The same on fp32 MFMA for 1 <= T <= kShortMfmaMaxT (dk % 16 == 0, dv % 64 == 0).
+constexpr int kShortMfmaMaxT = 32;
+constexpr int kShortMfmaMinT = 1;  // below this the VALU streaming kernel is used
+bool short_mfma_supports(int T, int dk, int dv);
+hipError_t launch_short_mfma(const void* q, const void* k, const void* v, const float* state_in, float* state_out,
+                             void* y, int B, int H, int T, int dk, int dv, int dt, const HeadGroup& g, hipStream_t s);
+
 // Copies state_in (or zeros when null) into state_out: the T = 0 case.
 hipError_t launch_state_copy(const float* state_in, float* state_out, size_t n, hipStream_t s);
 

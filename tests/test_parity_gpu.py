@@ -112,7 +112,7 @@ def test_chunkwise_vs_oracle(B, H, T, dk, dv, C, dt, with_state, gs):
     check("state_out", s, s_ref, bound)
 
 
-# ------------------------------------- short blocks (T <= 16): streaming kernel
+# ----------------------- short blocks (T <= 32): streaming kernels (fp32 MFMA / VALU)
 SHORT_CASES = [
     # B, H, T, dk, dv, dtype, state_in, state_out ("new" / "inplace" / None), gammas
     (2, 3, 1, 64, 128, "f32", True, "new", [0.0, 0.9, 1.0]),
@@ -128,12 +128,17 @@ SHORT_CASES = [
     (2, 2, 6, 64, 192, "bf16", True, "new", [0.0, 0.8]),
     (1, 2, 16, 128, 256, "bf16", False, "new", [0.99, 0.5]),
     (1, 2, 13, 100, 301, "bf16", True, "inplace", [0.7, 1.0]),
+    # 17..32 tokens (two 16-token blocks on the fp32 MFMA streaming kernel)
+    (1, 2, 17, 64, 64, "f32", True, "new", [0.0, 0.9]),
+    (2, 2, 32, 256, 512, "bf16", True, "inplace", [0.99, 1.0]),
+    (1, 3, 25, 128, 128, "f32", False, "new", [0.5, 0.8, 0.999]),
+    (1, 2, 29, 48, 192, "bf16", True, None, [0.95, 0.6]),
 ]
 
 
 @pytest.mark.parametrize("B,H,T,dk,dv,dt,with_in,out,gs", SHORT_CASES)
 def test_short_block_vs_oracle(B, H, T, dk, dv, dt, with_in, out, gs):
-    """Blocks of at most 16 tokens take the one-pass streaming kernel (any C):
+    """Blocks of at most 32 tokens take a one-pass streaming kernel (any C):
     y and the carried state against the oracle, with state_in absent or given,
     state_out absent, separate or the same buffer as state_in."""
     say(f"short block B{B} H{H} T{T} dk{dk} dv{dv} {dt} state_in={with_in} state_out={out}")
