@@ -7,7 +7,8 @@
 //   out[c] = (y[c] - mu) / sqrt(var + eps) * weight[h,c] + bias[h,c].
 // The pass streams y once in and once out, so it is bound by HBM bandwidth:
 // each row (token-head) is held by one wave, each lane holding its VEC-element
-// pieces in registers (one 16-byte load per lane for bf16 rows of 512), mean
+// pieces in registers (one 16-byte non-temporal load per lane for bf16 rows of
+// 512; y is read once and the output is not read back here), mean
 // and variance in two passes over the registers with wave-wide butterfly
 // sums, fp32 arithmetic throughout.
 #include "common.h"
@@ -25,7 +26,7 @@ template <>
 struct Vec<uint16_t, 8> {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   __device__ __forceinline__ static void load(const uint16_t* p, float (&x)[8]) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       x[2 * i] = __uint_as_float(v[i] << 16);
@@ -37,18 +38,18 @@ struct Vec<uint16_t, 8> {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       v[i] = static_cast<uint32_t>(f32_to_bf16(x[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(x[2 * i + 1])) << 16);
-    *reinterpret_cast<u32x4*>(p) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
   }
 };
 template <>
 struct Vec<float, 4> {
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   __device__ __forceinline__ static void load(const float* p, float (&x)[4]) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
     x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
   }
   __device__ __forceinline__ static void store(float* p, const float (&x)[4]) {
-    *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(p));
   }
 };
 template <typename E>
