@@ -93,6 +93,9 @@ CHUNK_CASES = [
     (1, 1, 4097, 256, 64, 128, "bf16", True, [0.999]),
     (1, 1, 1024, 64, 64, 1, "bf16", False, [0.97]),
     (1, 2, 2500, 256, 128, 100, "bf16", False, [1.0, 0.0]),
+    # segments together with more than 128 heads (two head-group launches
+    # sharing one workspace indexed by global head)
+    (1, 130, 1024, 64, 64, 64, "bf16", True, None),
 ]
 
 
@@ -190,6 +193,7 @@ BWD_CASES = [
     (1, 1, 4096, 64, 64, 64, "bf16", True, True, [0.999]),
     (1, 2, 3001, 128, 256, 64, "bf16", True, True, [0.995, 0.9]),
     (1, 1, 2500, 256, 512, 128, "bf16", False, False, [1.0]),
+    (1, 130, 1024, 64, 64, 64, "bf16", True, True, None),
 ]
 
 
