@@ -448,7 +448,13 @@ hipError_t launch_chunkwise_bwd_mfma(const BwdArgs& a, int B, int H, int T, int 
   hipError_t e = launch_by_da(dv, kq, B, hd, H, g, T, s);
   if (e != hipSuccess) return e;
   // dV (reverse over K, Q, dY from dS_out); final state = dS_in.  After the dK
-  // pass, so that dstate_in may be the dstate_out buffer.
+  // pass, so that dstate_in may be the dstate_out buffer.  It has the shape of
+  // the forward pass (d_a = dk, 64-column tiles of dY), so where the forward
+  // kernel's reverse mode takes it (and its segments fit the dV slots) it
+  // runs there.
+  const ChunkSegments sf = chunkwise_mfma_segments(B, H, T, dv, kRevChunk);
+  if (chunkwise_mfma_rev_supports(dk, dv, g) && (sf.nseg == 1 || sf.nseg <= sg.nseg))
+    return launch_chunkwise_mfma_rev(a.k, a.q, a.dy, a.dstate_out, a.dstate_in, a.dv, B, H, T, dk, dv, sf, wv, g, s);
   MPassSet vs{};
   vs.p[0] = MPass{u(a.k), u(a.q), u(a.dy), static_cast<uint16_t*>(a.dv), a.dstate_out, a.dstate_in, 0, 1, dv, wv,
                   stride};

@@ -93,7 +93,16 @@ struct SegArgs {
 // gamma^(CT-1) >= 2^-100 (the host checks this for every head of the launch).
 // kZS = false keeps V unscaled and applies zeta to the update's operand in
 // registers (any gamma in [0, 1]).
-template <int CT, int DK, bool kOut, bool kZS>
+// kRev = true: the same pass backwards in time with the decay weights shifted
+// by one token, the shape of the value gradient of the chunkwise form (chain
+// rule on the recurrence of the aimpact page, "Il meccanismo"):
+//   position p counts from the end (token Tn-1-p), and for chunk rows j
+//   Y_j = gamma^j Q_j R + sum_{t<=j} gamma^(j-t) (Q_j . K_t) V_t
+//   R  <- gamma^L R + sum_t gamma^(L-t) K_t^T V_t
+// i.e. zeta_t = gamma^(L-t) and gamma^j in place of gamma^(j+1); with
+// Q, K, V, R_0 = (K, Q, dY, dS_out) the outputs are dV and the final state is
+// dS_in.  Only with kZS (the host checks gamma^CT >= 2^-100).
+template <int CT, int DK, bool kOut, bool kZS, bool kRev>
 __global__ __attribute__((amdgpu_flat_work_group_size(kOut ? 512 : 256, kOut ? 512 : 256),
                           amdgpu_waves_per_eu(kOut ? 2 : 1, 2))) void
 chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -101,7 +110,9 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                       uint16_t* __restrict__ y, HeadDecay gam, int H, int h0, int nh, int Tn, int dv, int C,
                       int ntiles, SegArgs sg) {
   using F = Cfg<CT, DK>;
+  static_assert(!kRev || kZS, "the reverse pass stages zeta V");
   constexpr int NSP = CT / 32;  // key (token) steps of 32 per chunk tile
+  constexpr int kShift = kRev ? 1 : 0;  // decay exponent shift of the reverse pass
   constexpr int NB = F::NBUF;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[NB][CT * F::KLD];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[NB][CT * F::VLD];
@@ -142,6 +153,19 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const int t_begin = seg * sg.seg_len;
   const int t_end = min(Tn, t_begin + sg.seg_len);
   const int nchunks = (t_end - t_begin + C - 1) / C;
+  // Row addressing of the chunk at position s with L valid rows.  A buffer
+  // resource starts at row first_row(s, L) and spans L rows; tile row r sits
+  // at row_off(r) in it.  Forward: tokens s..s+L-1 in order.  Reverse: the
+  // tokens Tn-s-L..Tn-s-1 read last to first; rows r >= L map past every
+  // buffer's end (0x80000000 > any span), so they read as zero and their
+  // stores are dropped, as rows past the span do in the forward direction.
+  auto first_row = [&](int s, int L) __attribute__((always_inline)) {
+    return kRev ? max(0, Tn - s - L) : s;
+  };
+  auto row_off = [&](int r, int L, uint32_t row_bytes) __attribute__((always_inline)) -> uint32_t {
+    if constexpr (kRev) return r < L ? static_cast<uint32_t>(L - 1 - r) * row_bytes : 0x80000000u;
+    return static_cast<uint32_t>(r) * row_bytes;
+  };
 
   // fp32 state tile in and out.  init: state_in (one segment), the scanned
   // slot of this segment, or zero (state-only pass); fin: state_out (last
@@ -225,14 +249,17 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     using I1 = std::integral_constant<int, 1>;
     auto load_kv = [&](auto set_c, int s1, int Ln) __attribute__((always_inline)) {
       constexpr int set = decltype(set_c)::value;
-      const rsrc_t rk = make_rsrc(kh + static_cast<long>(s1) * DK, static_cast<uint32_t>(Ln) * DK * 2u);
+      const int r0 = first_row(s1, Ln);
+      const rsrc_t rk = make_rsrc(kh + static_cast<long>(r0) * DK, static_cast<uint32_t>(Ln) * DK * 2u);
 #pragma unroll
       for (int r = 0; r < F::KPT; ++r)
-        kreg[set][r] = buffer_load16(rk, koff + static_cast<uint32_t>(r * KRR * DK * 2));
-      const rsrc_t rv = make_rsrc(vh + static_cast<long>(s1) * dv,
+        kreg[set][r] = buffer_load16(rk, kRev ? row_off(krow + r * KRR, Ln, DK * 2u) + 16u * kc8
+                                              : koff + static_cast<uint32_t>(r * KRR * DK * 2));
+      const rsrc_t rv = make_rsrc(vh + static_cast<long>(r0) * dv,
                                   Ln > 0 ? static_cast<uint32_t>(Ln - 1) * vrow + kTN * 2u : 0u);
 #pragma unroll
-      for (int r = 0; r < F::VPT; ++r) vreg[set][r] = buffer_load16(rv, voff + 32u * vrow * r);
+      for (int r = 0; r < F::VPT; ++r)
+        vreg[set][r] = buffer_load16(rv, kRev ? row_off(prow + 32 * r, Ln, vrow) + 16u * vc8 : voff + 32u * vrow * r);
     };
     // Ln: length of the chunk being staged (zeta of its rows when kZS)
     auto store_kv = [&](auto set_c, int buf, int Ln) __attribute__((always_inline)) {
@@ -244,7 +271,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       for (int r = 0; r < F::VPT; ++r) {
         const int row = prow + 32 * r;
         if constexpr (kZS) {
-          const float z = row < Ln ? gamma_pow(lg, Ln - 1 - row) : 0.0f;
+          const float z = row < Ln ? gamma_pow(lg, Ln - 1 - row + kShift) : 0.0f;
           const f32x8 vf = __builtin_convertvector(__builtin_bit_cast(bf16x8, vreg[set][r]), f32x8) * z;
           *reinterpret_cast<bf16x8*>(&Vs[buf][row * F::VLD + 8 * vc8]) = __builtin_convertvector(vf, bf16x8);
         } else {
@@ -451,10 +478,10 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     typedef bf16x8 QTile[F::NQ][F::KS];
     QTile Qa, Qb;
     auto load_q = [&](QTile& Qd, int s1, int Ln) __attribute__((always_inline)) {
-      const rsrc_t rq = make_rsrc(qh + static_cast<long>(s1) * DK, static_cast<uint32_t>(Ln) * DK * 2u);
+      const rsrc_t rq = make_rsrc(qh + static_cast<long>(first_row(s1, Ln)) * DK, static_cast<uint32_t>(Ln) * DK * 2u);
 #pragma unroll
       for (int qi = 0; qi < F::NQ; ++qi) {
-        const uint32_t rowoff = static_cast<uint32_t>(16 * (qi == 0 ? W : QB1) + c16) * DK * 2u + 16u * g;
+        const uint32_t rowoff = row_off(16 * (qi == 0 ? W : QB1) + c16, Ln, DK * 2u) + 16u * g;
 #pragma unroll
         for (int s = 0; s < F::KS; ++s) Qd[qi][s] = __builtin_bit_cast(bf16x8, buffer_load16(rq, rowoff + 64u * s));
       }
@@ -538,7 +565,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       float xi[F::NQ];
 #pragma unroll
       for (int qi = 0; qi < F::NQ; ++qi) {
-        xi[qi] = gamma_pow(lg, 16 * (qi == 0 ? W : QB1) + c16 + 1);
+        xi[qi] = gamma_pow(lg, 16 * (qi == 0 ? W : QB1) + c16 + 1 - kShift);
         if constexpr (!kZS) {
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb) O[qi][nb] *= xi[qi];
@@ -593,10 +620,11 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       // store Y rows, 4 columns (8 bytes) per lane and block (rows past the
       // chunk end fall outside the buffer and are dropped)
       {
-        const rsrc_t ry = make_rsrc(yh + static_cast<long>(s0) * dv, static_cast<uint32_t>(L - 1) * vrow + kTN * 2u);
+        const rsrc_t ry = make_rsrc(yh + static_cast<long>(first_row(s0, L)) * dv,
+                                    static_cast<uint32_t>(L - 1) * vrow + kTN * 2u);
 #pragma unroll
         for (int qi = 0; qi < F::NQ; ++qi) {
-          const uint32_t roff = static_cast<uint32_t>(16 * (qi == 0 ? W : QB1) + c16) * vrow + 8u * g;
+          const uint32_t roff = row_off(16 * (qi == 0 ? W : QB1) + c16, L, vrow) + 8u * g;
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb) {
             const bf16x4 o = __builtin_convertvector(kZS ? O[qi][nb] * xi[qi] : O[qi][nb], bf16x4);
@@ -650,7 +678,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ w
   }
 }
 
-template <int CT, int DK, bool kZS>
+template <int CT, int DK, bool kZS, bool kRev>
 hipError_t launch_cfg(const void* q, const void* k, const void* v, const float* state_in, float* state_out, void* y,
                       int B, int H, int Tn, int dv, int C, const HeadDecay& hd, const HeadGroup& g,
                       const ChunkSegments& segs, float* ws, hipStream_t s) {
@@ -663,7 +691,7 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, const float* 
   uint16_t* yp = static_cast<uint16_t*>(y);
   if (segs.nseg > 1) {
     // end states of segments 0..nseg-2 from zero, then the scan over segments
-    hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, false, kZS>), dim3(bnh * ntiles * (segs.nseg - 1)), dim3(256), 0, s,
+    hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, false, kZS, kRev>), dim3(bnh * ntiles * (segs.nseg - 1)), dim3(256), 0, s,
                        qp, kp, vp, nullptr, nullptr, yp, hd, H, g.h0, g.nh, Tn, dv, C, ntiles, sg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -675,19 +703,19 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, const float* 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, true, kZS>), dim3(bnh * ntiles * segs.nseg), dim3(512), 0, s, qp, kp, vp,
+  hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, true, kZS, kRev>), dim3(bnh * ntiles * segs.nseg), dim3(512), 0, s, qp, kp, vp,
                      state_in, state_out, yp, hd, H, g.h0, g.nh, Tn, dv, C, ntiles, sg);
   return hipGetLastError();
 }
 
-template <int CT, bool kZS>
+template <int CT, bool kZS, bool kRev = false>
 hipError_t launch_ct(const void* q, const void* k, const void* v, const float* state_in, float* state_out, void* y,
                      int B, int H, int Tn, int dk, int dv, int C, const HeadDecay& hd, const HeadGroup& g,
                      const ChunkSegments& segs, float* ws, hipStream_t s) {
   switch (dk) {
-    case 64: return launch_cfg<CT, 64, kZS>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
-    case 128: return launch_cfg<CT, 128, kZS>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
-    default: return launch_cfg<CT, 256, kZS>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
+    case 64: return launch_cfg<CT, 64, kZS, kRev>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
+    case 128: return launch_cfg<CT, 128, kZS, kRev>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
+    default: return launch_cfg<CT, 256, kZS, kRev>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
   }
 }
 
@@ -730,6 +758,22 @@ hipError_t launch_chunkwise_mfma(const void* q, const void* k, const void* v, co
   }
   if (zs) return launch_ct<128, true>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, hd, g, segs, ws, s);
   return launch_ct<128, false>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, hd, g, segs, ws, s);
+}
+
+bool chunkwise_mfma_rev_supports(int dk, int dv, const HeadGroup& g) {
+  if (!chunkwise_mfma_supports(0, dk, dv, kRevChunk, 1)) return false;
+  const HeadDecay hd = make_head_decay(g);
+  for (int i = 0; i < g.nh; ++i)
+    if (!(static_cast<double>(kRevChunk) * hd.log2g[i] >= -100.0)) return false;  // zeta = gamma^(L-t) >= gamma^CT
+  return true;
+}
+
+hipError_t launch_chunkwise_mfma_rev(const void* q, const void* k, const void* v, const float* state_in,
+                                     float* state_out, void* y, int B, int H, int T, int dk, int dv,
+                                     const ChunkSegments& segs, float* ws, const HeadGroup& g, hipStream_t s) {
+  const HeadDecay hd = make_head_decay(g);
+  return launch_ct<kRevChunk, true, true>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, kRevChunk, hd, g, segs,
+                                          ws, s);
 }
 
 }  // namespace ret

@@ -49,6 +49,20 @@ hipError_t launch_chunkwise_mfma(const void* q, const void* k, const void* v, co
                                  float* state_out, void* y, int B, int H, int T, int dk, int dv, int C,
                                  const ChunkSegments& segs, float* ws, const HeadGroup& g, hipStream_t s);
 
+// The same kernel backwards in time with the decay weights of the value
+// gradient: for position p = Tn-1-n (n the token) and chunk rows j,
+//   Y_j = gamma^j Q_j R + sum_{t<=j} gamma^(j-t) (Q_j . K_t) V_t,
+//   R <- gamma^L R + sum_t gamma^(L-t) K_t^T V_t,
+// in chunks of kRevChunk positions.  With (Q, K, V, R_0) = (K, Q, dY, dS_out)
+// it writes dV and its final state is dS_in.  Segments as for the forward
+// (chunkwise_mfma_segments with C = kRevChunk).  Needs gamma^kRevChunk >=
+// 2^-100 for every head (chunkwise_mfma_rev_supports).
+constexpr int kRevChunk = 64;
+bool chunkwise_mfma_rev_supports(int dk, int dv, const HeadGroup& g);
+hipError_t launch_chunkwise_mfma_rev(const void* q, const void* k, const void* v, const float* state_in,
+                                     float* state_out, void* y, int B, int H, int T, int dk, int dv,
+                                     const ChunkSegments& segs, float* ws, const HeadGroup& g, hipStream_t s);
+
 // Streaming chunkwise kernel for a short block of tokens from a carried state
 // (1 <= T <= kShortChunkMaxT, fp32 or bf16 inputs, any supported dk and dv):
 // the whole block is one chunk, and the state is read and written once.
