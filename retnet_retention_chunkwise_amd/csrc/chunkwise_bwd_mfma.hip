@@ -438,15 +438,23 @@ hipError_t launch_chunkwise_bwd_mfma(const BwdArgs& a, int B, int H, int T, int 
   float* wk = sg.nseg > 1 ? ws + sg.nseg * stride : nullptr;
   float* wq = sg.nseg > 1 ? ws + 2 * sg.nseg * stride : nullptr;
   // dK (reverse over V, dY, Q from dS_out^T) and dQ (forward over dY, V, K from
-  // S_in^T) share d_a = dv: one launch
-  MPassSet kq{};
-  kq.p[0] = MPass{u(a.v), u(a.dy), u(a.q), static_cast<uint16_t*>(a.dk), a.dstate_out, nullptr, 1, 1, dk, wk, stride};
-  kq.p[1] = MPass{u(a.dy), u(a.v), u(a.k), static_cast<uint16_t*>(a.dq), a.state_in, nullptr, 1, 0, dk, wq, stride};
-  kq.npass = 2;
-  kq.nseg = sg.nseg;
-  kq.seg_len = sg.seg_len;
-  hipError_t e = launch_by_da(dv, kq, B, hd, H, g, T, s);
-  if (e != hipSuccess) return e;
+  // S_in^T) share d_a = dv: one launch.  Unsegmented, they run as a pass pair
+  // on the forward kernel (64-column tiles of Q and K) where it takes them.
+  if (sg.nseg == 1 && T > 0 && chunkwise_mfma_pair_supports(dv, dk, g)) {
+    const ChunkPass pk{a.v, a.dy, a.q, a.dstate_out, 1, 1, nullptr, a.dk};
+    const ChunkPass pq{a.dy, a.v, a.k, a.state_in, 1, 0, nullptr, a.dq};
+    const hipError_t e = launch_chunkwise_mfma_pair(pk, pq, B, H, T, dv, dk, g, s);
+    if (e != hipSuccess) return e;
+  } else {
+    MPassSet kq{};
+    kq.p[0] = MPass{u(a.v), u(a.dy), u(a.q), static_cast<uint16_t*>(a.dk), a.dstate_out, nullptr, 1, 1, dk, wk, stride};
+    kq.p[1] = MPass{u(a.dy), u(a.v), u(a.k), static_cast<uint16_t*>(a.dq), a.state_in, nullptr, 1, 0, dk, wq, stride};
+    kq.npass = 2;
+    kq.nseg = sg.nseg;
+    kq.seg_len = sg.seg_len;
+    const hipError_t e = launch_by_da(dv, kq, B, hd, H, g, T, s);
+    if (e != hipSuccess) return e;
+  }
   // dV (reverse over K, Q, dY from dS_out); final state = dS_in.  After the dK
   // pass, so that dstate_in may be the dstate_out buffer.  It has the shape of
   // the forward pass (d_a = dk, 64-column tiles of dY), so where the forward

@@ -93,26 +93,37 @@ struct SegArgs {
 // gamma^(CT-1) >= 2^-100 (the host checks this for every head of the launch).
 // kZS = false keeps V unscaled and applies zeta to the update's operand in
 // registers (any gamma in [0, 1]).
-// kRev = true: the same pass backwards in time with the decay weights shifted
-// by one token, the shape of the value gradient of the chunkwise form (chain
-// rule on the recurrence of the aimpact page, "Il meccanismo"):
-//   position p counts from the end (token Tn-1-p), and for chunk rows j
+// Direction (kDir): 0 = forward in time.  1 = the same pass backwards in time
+// with the decay weights shifted by one token, the shape of the gradient
+// passes of the chunkwise form (chain rule on the recurrence of the aimpact
+// page, "Il meccanismo"): position p counts from the end (token Tn-1-p), and
+// for chunk rows j
 //   Y_j = gamma^j Q_j R + sum_{t<=j} gamma^(j-t) (Q_j . K_t) V_t
 //   R  <- gamma^L R + sum_t gamma^(L-t) K_t^T V_t
 // i.e. zeta_t = gamma^(L-t) and gamma^j in place of gamma^(j+1); with
-// Q, K, V, R_0 = (K, Q, dY, dS_out) the outputs are dV and the final state is
-// dS_in.  Only with kZS (the host checks gamma^CT >= 2^-100).
-template <int CT, int DK, bool kOut, bool kZS, bool kRev>
+// (Q, K, V, R_0) = (K, Q, dY, dS_out) the outputs are dV and the final state
+// is dS_in, with (V, dY, Q, dS_out^T) they are dK.  2 = per pass (PassPtrs::rev),
+// for launches that run two passes (dQ forward and dK reverse).  The reverse
+// direction needs kZS (the host checks gamma^CT >= 2^-100).
+struct PassPtrs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* state_in;  // nullable
+  float* state_out;       // nullable
+  uint16_t* y;
+  int rev;         // reverse direction (kDir = 2)
+  int state_in_t;  // state_in stored transposed, [dv x DK] per head (one segment only)
+};
+
+template <int CT, int DK, bool kOut, bool kZS, int kDir>
 __global__ __attribute__((amdgpu_flat_work_group_size(kOut ? 512 : 256, kOut ? 512 : 256),
                           amdgpu_waves_per_eu(kOut ? 2 : 1, 2))) void
-chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                      const uint16_t* __restrict__ v, const float* state_in, float* state_out,
-                      uint16_t* __restrict__ y, HeadDecay gam, int H, int h0, int nh, int Tn, int dv, int C,
-                      int ntiles, SegArgs sg) {
+chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H, int h0, int nh, int Tn, int dv,
+                      int C, int ntiles, SegArgs sg) {
   using F = Cfg<CT, DK>;
-  static_assert(!kRev || kZS, "the reverse pass stages zeta V");
+  static_assert(kDir == 0 || kZS, "the reverse pass stages zeta V");
   constexpr int NSP = CT / 32;  // key (token) steps of 32 per chunk tile
-  constexpr int kShift = kRev ? 1 : 0;  // decay exponent shift of the reverse pass
   constexpr int NB = F::NBUF;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[NB][CT * F::KLD];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[NB][CT * F::VLD];
@@ -129,25 +140,30 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const int c16 = lane & 15;
   const int g = lane >> 4;
 
-  // Workgroup -> (segment, batch, head, column tile).  Consecutive linear ids
-  // (the column tiles of one head and segment) are placed on one XCD
-  // (dispatch is round-robin over the 8 XCDs by workgroup id).
+  // Workgroup -> (segment, batch, head, pass, column tile).  Consecutive
+  // linear ids (the column tiles and passes of one head and segment, which
+  // read the same rows) are placed on one XCD (dispatch is round-robin over
+  // the 8 XCDs by workgroup id).
   const int total = gridDim.x;
   int lin = blockIdx.x;
   if ((total & 7) == 0) lin = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
   const int tile = lin % ntiles;
-  const int bh = (lin / ntiles) % sg.bnh;
-  const int seg = lin / ntiles / sg.bnh;
+  const int pz = npass > 1 ? (lin / ntiles) % npass : 0;
+  const int bh = (lin / ntiles / npass) % sg.bnh;
+  const int seg = lin / ntiles / npass / sg.bnh;
+  const PassPtrs P = pz ? p1 : p0;
+  const bool rev = kDir == 2 ? P.rev != 0 : kDir == 1;
+  const int kShift = rev ? 1 : 0;  // decay exponent shift of the reverse direction
   const int hl = bh % nh;
   const int b = bh / nh;
   const long head = static_cast<long>(b) * H + h0 + hl;
   const int col0 = tile * kTN;
   const float lg = gam.log2g[hl];
 
-  const uint16_t* qh = q + head * Tn * DK;
-  const uint16_t* kh = k + head * Tn * DK;
-  const uint16_t* vh = v + head * Tn * dv + col0;
-  uint16_t* yh = y + head * Tn * dv + col0;
+  const uint16_t* qh = P.q + head * Tn * DK;
+  const uint16_t* kh = P.k + head * Tn * DK;
+  const uint16_t* vh = P.v + head * Tn * dv + col0;
+  uint16_t* yh = P.y + head * Tn * dv + col0;
   const long sbase = head * static_cast<long>(DK) * dv + col0;
   const uint32_t vrow = static_cast<uint32_t>(dv) * 2u;  // bytes per V / Y row
   const int t_begin = seg * sg.seg_len;
@@ -160,10 +176,10 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   // buffer's end (0x80000000 > any span), so they read as zero and their
   // stores are dropped, as rows past the span do in the forward direction.
   auto first_row = [&](int s, int L) __attribute__((always_inline)) {
-    return kRev ? max(0, Tn - s - L) : s;
+    return rev ? max(0, Tn - s - L) : s;
   };
   auto row_off = [&](int r, int L, uint32_t row_bytes) __attribute__((always_inline)) -> uint32_t {
-    if constexpr (kRev) return r < L ? static_cast<uint32_t>(L - 1 - r) * row_bytes : 0x80000000u;
+    if (rev) return r < L ? static_cast<uint32_t>(L - 1 - r) * row_bytes : 0x80000000u;
     return static_cast<uint32_t>(r) * row_bytes;
   };
 
@@ -173,8 +189,9 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   // [d_k x 64] tile moves through LDS (the K buffers, before the first chunk is
   // staged and after the last one is read), so that global accesses are whole
   // 256-byte rows; SRN rounds of SRR rows, two barriers per round in every wave.
-  const float* init = !kOut ? nullptr : (sg.nseg > 1 ? sg.ws + seg * sg.ws_stride : state_in);
-  float* fin = kOut ? (seg == sg.nseg - 1 ? state_out : nullptr) : sg.ws + (seg + 1) * sg.ws_stride;
+  const float* init = !kOut ? nullptr : (sg.nseg > 1 ? sg.ws + seg * sg.ws_stride : P.state_in);
+  const bool init_t = sg.nseg == 1 && P.state_in_t != 0;  // init is stored transposed
+  float* fin = kOut ? (seg == sg.nseg - 1 ? P.state_out : nullptr) : sg.ws + (seg + 1) * sg.ws_stride;
   constexpr int SLD = kTN + 4;                 // fp32 row stride in LDS
   constexpr int SRR = DK < 128 ? DK : 128;     // rows per round
   constexpr int SRN = DK / SRR;                // rounds
@@ -193,12 +210,26 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     if (init != nullptr) {
       for (int rr = 0; rr < SRN; ++rr) {
         const int r0 = rr * SRR;
-        // 16 lanes per 256-byte row, 16 rows per pass of the 256 staging threads
+        if (init_t) {
+          // element (row a, column x) of the head's state at x * DK + a: 16-byte
+          // reads along a, transposed into the LDS rows
+          const float* src = init + head * static_cast<long>(DK) * dv;
 #pragma unroll
-        for (int p = 0; p < SRR / 16; ++p) {
-          const int row = 16 * p + (st >> 4);
-          *reinterpret_cast<u32x4*>(&Sst[row * SLD + 4 * (st & 15)]) =
-              *reinterpret_cast<const u32x4*>(&init[sbase + static_cast<long>(r0 + row) * dv + 4 * (st & 15)]);
+          for (int p = 0; p < SRR / 16; ++p) {
+            const int idx = 256 * p + st;
+            const int x = idx / (SRR / 4), a4 = idx % (SRR / 4);
+            const u32x4 val = *reinterpret_cast<const u32x4*>(&src[static_cast<long>(col0 + x) * DK + r0 + 4 * a4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Sst[(4 * a4 + e) * SLD + x] = __uint_as_float(val[e]);
+          }
+        } else {
+          // 16 lanes per 256-byte row, 16 rows per pass of the 256 staging threads
+#pragma unroll
+          for (int p = 0; p < SRR / 16; ++p) {
+            const int row = 16 * p + (st >> 4);
+            *reinterpret_cast<u32x4*>(&Sst[row * SLD + 4 * (st & 15)]) =
+                *reinterpret_cast<const u32x4*>(&init[sbase + static_cast<long>(r0 + row) * dv + 4 * (st & 15)]);
+          }
         }
         lds_barrier();
 #pragma unroll
@@ -253,13 +284,13 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       const rsrc_t rk = make_rsrc(kh + static_cast<long>(r0) * DK, static_cast<uint32_t>(Ln) * DK * 2u);
 #pragma unroll
       for (int r = 0; r < F::KPT; ++r)
-        kreg[set][r] = buffer_load16(rk, kRev ? row_off(krow + r * KRR, Ln, DK * 2u) + 16u * kc8
-                                              : koff + static_cast<uint32_t>(r * KRR * DK * 2));
+        kreg[set][r] = buffer_load16(rk, rev ? row_off(krow + r * KRR, Ln, DK * 2u) + 16u * kc8
+                                             : koff + static_cast<uint32_t>(r * KRR * DK * 2));
       const rsrc_t rv = make_rsrc(vh + static_cast<long>(r0) * dv,
                                   Ln > 0 ? static_cast<uint32_t>(Ln - 1) * vrow + kTN * 2u : 0u);
 #pragma unroll
       for (int r = 0; r < F::VPT; ++r)
-        vreg[set][r] = buffer_load16(rv, kRev ? row_off(prow + 32 * r, Ln, vrow) + 16u * vc8 : voff + 32u * vrow * r);
+        vreg[set][r] = buffer_load16(rv, rev ? row_off(prow + 32 * r, Ln, vrow) + 16u * vc8 : voff + 32u * vrow * r);
     };
     // Ln: length of the chunk being staged (zeta of its rows when kZS)
     auto store_kv = [&](auto set_c, int buf, int Ln) __attribute__((always_inline)) {
@@ -410,9 +441,11 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         const int L = min(C, t_end - s0);
         const int s1 = s0 + C;
         const int Ln = clen(s1);
-        // next chunk's K/V, written after the barrier
-        load_kv(I0(), s1, Ln);
+        // next chunk's K/V, written after the barrier (d_k = 512: issued after
+        // the update, whose state and operand registers leave no room for them)
+        if constexpr (DK <= 256) load_kv(I0(), s1, Ln);
         update(0, L);
+        if constexpr (DK > 256) load_kv(I0(), s1, Ln);
         lds_barrier();  // output waves are done with R^T, K and V of this chunk
         if constexpr (kOut) write_rt(0);
         if (Ln > 0) {
@@ -474,7 +507,7 @@ chunkwise_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     // Q operand registers.  With one query block per wave there is room for
     // two copies: the next chunk's Q is loaded at the start of a chunk, a
     // whole chunk ahead of its use; otherwise it is loaded after the d_k pass.
-    constexpr bool kQ2 = F::NQ == 1;
+    constexpr bool kQ2 = F::NQ == 1 && DK <= 256;
     typedef bf16x8 QTile[F::NQ][F::KS];
     QTile Qa, Qb;
     auto load_q = [&](QTile& Qd, int s1, int Ln) __attribute__((always_inline)) {
@@ -678,21 +711,19 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ w
   }
 }
 
-template <int CT, int DK, bool kZS, bool kRev>
+template <int CT, int DK, bool kZS, int kDir>
 hipError_t launch_cfg(const void* q, const void* k, const void* v, const float* state_in, float* state_out, void* y,
                       int B, int H, int Tn, int dv, int C, const HeadDecay& hd, const HeadGroup& g,
                       const ChunkSegments& segs, float* ws, hipStream_t s) {
   const int ntiles = dv / kTN;
   const int bnh = B * g.nh;
   SegArgs sg{segs.seg_len, segs.nseg, bnh, ws, static_cast<long>(B) * H * DK * dv};
-  const uint16_t* qp = static_cast<const uint16_t*>(q);
-  const uint16_t* kp = static_cast<const uint16_t*>(k);
-  const uint16_t* vp = static_cast<const uint16_t*>(v);
-  uint16_t* yp = static_cast<uint16_t*>(y);
+  const PassPtrs pp{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                    state_in, state_out, static_cast<uint16_t*>(y), kDir == 1, 0};
   if (segs.nseg > 1) {
     // end states of segments 0..nseg-2 from zero, then the scan over segments
-    hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, false, kZS, kRev>), dim3(bnh * ntiles * (segs.nseg - 1)), dim3(256), 0, s,
-                       qp, kp, vp, nullptr, nullptr, yp, hd, H, g.h0, g.nh, Tn, dv, C, ntiles, sg);
+    hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, false, kZS, kDir>), dim3(bnh * ntiles * (segs.nseg - 1)), dim3(256),
+                       0, s, pp, pp, 1, hd, H, g.h0, g.nh, Tn, dv, C, ntiles, sg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long per_head = static_cast<long>(DK) * dv;
@@ -703,20 +734,33 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, const float* 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, true, kZS, kRev>), dim3(bnh * ntiles * segs.nseg), dim3(512), 0, s, qp, kp, vp,
-                     state_in, state_out, yp, hd, H, g.h0, g.nh, Tn, dv, C, ntiles, sg);
+  hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, true, kZS, kDir>), dim3(bnh * ntiles * segs.nseg), dim3(512), 0, s, pp,
+                     pp, 1, hd, H, g.h0, g.nh, Tn, dv, C, ntiles, sg);
   return hipGetLastError();
 }
 
-template <int CT, bool kZS, bool kRev = false>
+template <int CT, bool kZS, int kDir = 0>
 hipError_t launch_ct(const void* q, const void* k, const void* v, const float* state_in, float* state_out, void* y,
                      int B, int H, int Tn, int dk, int dv, int C, const HeadDecay& hd, const HeadGroup& g,
                      const ChunkSegments& segs, float* ws, hipStream_t s) {
   switch (dk) {
-    case 64: return launch_cfg<CT, 64, kZS, kRev>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
-    case 128: return launch_cfg<CT, 128, kZS, kRev>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
-    default: return launch_cfg<CT, 256, kZS, kRev>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
+    case 64: return launch_cfg<CT, 64, kZS, kDir>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
+    case 128: return launch_cfg<CT, 128, kZS, kDir>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
+    default: return launch_cfg<CT, 256, kZS, kDir>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
   }
+}
+
+// Two passes of one d_a (= DK) and X width in one launch, one segment: the
+// column tiles of both passes of a head are adjacent work items (one XCD).
+template <int DK>
+hipError_t launch_pair_dk(const PassPtrs& a, const PassPtrs& b, int B, int H, int Tn, int dx, const HeadDecay& hd,
+                          const HeadGroup& g, hipStream_t s) {
+  const int ntiles = dx / kTN;
+  const int bnh = B * g.nh;
+  const SegArgs sg{Tn, 1, bnh, nullptr, 0};
+  hipLaunchKernelGGL((chunkwise_mfma_kernel<kRevChunk, DK, true, true, 2>), dim3(bnh * ntiles * 2), dim3(512), 0, s, a,
+                     b, 2, hd, H, g.h0, g.nh, Tn, dx, kRevChunk, ntiles, sg);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -768,11 +812,36 @@ bool chunkwise_mfma_rev_supports(int dk, int dv, const HeadGroup& g) {
   return true;
 }
 
+bool chunkwise_mfma_pair_supports(int da, int dx, const HeadGroup& g) {
+  if (!(da == 64 || da == 128 || da == 256 || da == 512) || dx % kTN != 0) return false;
+  const HeadDecay hd = make_head_decay(g);
+  for (int i = 0; i < g.nh; ++i)
+    if (!(static_cast<double>(kRevChunk) * hd.log2g[i] >= -100.0)) return false;
+  return true;
+}
+
+hipError_t launch_chunkwise_mfma_pair(const ChunkPass& a, const ChunkPass& b, int B, int H, int T, int da, int dx,
+                                      const HeadGroup& g, hipStream_t s) {
+  const HeadDecay hd = make_head_decay(g);
+  auto pp = [](const ChunkPass& c) {
+    return PassPtrs{static_cast<const uint16_t*>(c.q), static_cast<const uint16_t*>(c.k),
+                    static_cast<const uint16_t*>(c.v), c.state_in, c.state_out, static_cast<uint16_t*>(c.y), c.rev,
+                    c.state_in_t};
+  };
+  const PassPtrs pa = pp(a), pb = pp(b);
+  switch (da) {
+    case 64: return launch_pair_dk<64>(pa, pb, B, H, T, dx, hd, g, s);
+    case 128: return launch_pair_dk<128>(pa, pb, B, H, T, dx, hd, g, s);
+    case 256: return launch_pair_dk<256>(pa, pb, B, H, T, dx, hd, g, s);
+    default: return launch_pair_dk<512>(pa, pb, B, H, T, dx, hd, g, s);
+  }
+}
+
 hipError_t launch_chunkwise_mfma_rev(const void* q, const void* k, const void* v, const float* state_in,
                                      float* state_out, void* y, int B, int H, int T, int dk, int dv,
                                      const ChunkSegments& segs, float* ws, const HeadGroup& g, hipStream_t s) {
   const HeadDecay hd = make_head_decay(g);
-  return launch_ct<kRevChunk, true, true>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, kRevChunk, hd, g, segs,
+  return launch_ct<kRevChunk, true, 1>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, kRevChunk, hd, g, segs,
                                           ws, s);
 }
 

@@ -63,6 +63,25 @@ hipError_t launch_chunkwise_mfma_rev(const void* q, const void* k, const void* v
                                      float* state_out, void* y, int B, int H, int T, int dk, int dv,
                                      const ChunkSegments& segs, float* ws, const HeadGroup& g, hipStream_t s);
 
+// Two passes of that kernel in one launch (one segment, chunks of kRevChunk,
+// T >= 1): each pass forward or reverse in time, its initial state optionally
+// stored transposed ([dx, da] per head), bf16 inputs, d_a in {64, 128, 256,
+// 512}, dx % 64 == 0.  dQ (forward over dY, V, K from S_in^T) and dK (reverse
+// over V, dY, Q from dS_out^T) take it.
+struct ChunkPass {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* state_in;  // nullable
+  int state_in_t;
+  int rev;
+  float* state_out;  // nullable
+  void* y;
+};
+bool chunkwise_mfma_pair_supports(int da, int dx, const HeadGroup& g);
+hipError_t launch_chunkwise_mfma_pair(const ChunkPass& a, const ChunkPass& b, int B, int H, int T, int da, int dx,
+                                      const HeadGroup& g, hipStream_t s);
+
 // Streaming chunkwise kernel for a short block of tokens from a carried state
 // (1 <= T <= kShortChunkMaxT, fp32 or bf16 inputs, any supported dk and dv):
 // the whole block is one chunk, and the state is read and written once.
