@@ -273,20 +273,35 @@ def main():
     bq, bk, bv, bs0 = make_inputs(wl.B, wl.H, wl.T, wl.dk, wl.dv, wl.dtype, seed=7, with_state=True)
     _, _, bdy, bds = make_inputs(wl.B, wl.H, wl.T, wl.dk, wl.dv, wl.dtype, seed=8, with_state=True)
     bq, bk, bv, bs0, bdy, bds = (t.to(dev) for t in (bq, bk, bv, bs0, bdy, bds))
-    for _ in range(3):
+    for _ in range(10):
         ret.chunkwise_bwd(bq, bk, bv, g, wl.C, bdy, state_in=bs0, grad_state_out=bds)
     torch.cuda.synchronize()
-    bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
     for a, b in bev:
         a.record(stream)
         ret.chunkwise_bwd(bq, bk, bv, g, wl.C, bdy, state_in=bs0, grad_state_out=bds)
         b.record(stream)
     torch.cuda.synchronize()
-    bwd_us = statistics.median(a.elapsed_time(b) for a, b in bev) * 1e3
+    bwd_us_pairs = statistics.median(a.elapsed_time(b) for a, b in bev) * 1e3
+    # as for the forward: calls captured in a HIP graph and replayed back to
+    # back (one untimed replay first); the event pairs above also hold the
+    # host's work between the launches of a call
+    nbg = 20
+    bgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(bgraph):
+        for _ in range(nbg):
+            ret.chunkwise_bwd(bq, bk, bv, g, wl.C, bdy, state_in=bs0, grad_state_out=bds)
+    bgraph.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    bgraph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    bwd_us = e0.elapsed_time(e1) * 1e3 / nbg
+    del bgraph
     bwd_bytes = head_tokens * (2 * wl.dk * 2 + 2 * wl.dv * 2 + 2 * wl.dk * 2 + wl.dv * 2)  # q,k,v,dy in; dq,dk,dv out
     bwd_flops = 3 * alg_flops  # three chunkwise passes of the forward's per-token work
-    bwd_src = os.path.join(ROOT, "retnet_retention_chunkwise_amd", "csrc", "chunkwise_bwd_mfma.hip")
-    bwd_traffic = load_traffic("chunkwise_bwd_mfma_layer1p3b_traffic.txt", bwd_src)
+    bwd_traffic = load_traffic("chunkwise_mfma_bwd_passes_layer1p3b_traffic.txt", kernel_src)
     del bq, bk, bv, bs0, bdy, bds
     torch.cuda.empty_cache()
 
@@ -335,7 +350,7 @@ def main():
             "unit": "GB/s",
             "frac": achieved_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": "chunkwise_mfma_kernel<64, 256, true, true> (64-token tile, d_k 256, zeta-staged V)",
+            "kernel": "chunkwise_mfma_kernel<64, 256, true, true, 0> (64-token tile, d_k 256, zeta-staged V, forward in time)",
             "kernel_us": kernel_ms * 1e3,
             "kernel_us_event_pairs": kernel_ms_pairs * 1e3,
             "algorithmic_bytes_per_launch": alg_bytes,
@@ -368,6 +383,7 @@ def main():
                     "dv=512 bf16 C=64, with state_in and grad_state_out",
         "tokens_per_s": tokens / (bwd_us * 1e-6),
         "kernel_us": bwd_us,
+        "kernel_us_event_pairs": bwd_us_pairs,
         "roofline": {"bound": "hbm", "achieved": bwd_bytes / (bwd_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": bwd_bytes / (bwd_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
                      "traffic": bwd_traffic, "algorithmic_bytes_per_launch": bwd_bytes,

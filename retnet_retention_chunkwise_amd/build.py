@@ -30,7 +30,7 @@ SOURCES = [
     "state_copy.hip",
     "short_chunk.hip",
     "chunkwise_bwd.hip",
-    "chunkwise_bwd_mfma.hip",
+    "chunkwise_bwd_passes.cpp",
     "group_norm.hip",
     "chunkwise_f32_mfma.hip",
     "short_mfma.hip",

@@ -69,17 +69,29 @@ struct Cfg {
   static_assert(KPT >= 1 && VPT >= 1, "tile too small for the staging split");
 };
 
-// Sequence segments (long sequences with few heads).  Segment s covers tokens
-// [s*seg_len, (s+1)*seg_len).  ws holds nseg state slots of [B,H,dk,dv] fp32:
-// the state-only pass writes the end state of segment s (started from zero)
-// into slot s+1, the scan turns slot s into the incoming state of segment s,
-// and the full pass starts segment s from slot s.
+// Sequence segments (long sequences with few heads).  Segment s covers
+// positions [s*seg_len, (s+1)*seg_len).  Each pass's ws holds nseg state slots
+// of [B,H,dk,dv] fp32: the state-only pass writes the end state of segment s
+// (started from zero) into slot s+1, the scan turns slot s into the incoming
+// state of segment s, and the full pass starts segment s from slot s.
 struct SegArgs {
-  int seg_len;     // tokens per segment (a multiple of C)
+  int seg_len;     // positions per segment (a multiple of C)
   int nseg;        // segments; 1 = whole sequence, ws unused
   int bnh;         // B * heads of this launch
-  float* ws;       // workspace (nseg slots) or null
   long ws_stride;  // elements per slot (B * H * dk * dv)
+};
+
+// Pointers of one pass (the kernel takes one or two; see kDir).
+struct PassPtrs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* state_in;  // nullable
+  float* state_out;       // nullable
+  uint16_t* y;
+  int rev;         // reverse direction (kDir = 2)
+  int state_in_t;  // state_in stored transposed, [dv x DK] per head (read by the scan when segmented)
+  float* ws;       // segment slots (nseg > 1) or null
 };
 
 // kOut = true: the full kernel (outputs and state, 4 + 4 waves).
@@ -103,18 +115,8 @@ struct SegArgs {
 // i.e. zeta_t = gamma^(L-t) and gamma^j in place of gamma^(j+1); with
 // (Q, K, V, R_0) = (K, Q, dY, dS_out) the outputs are dV and the final state
 // is dS_in, with (V, dY, Q, dS_out^T) they are dK.  2 = per pass (PassPtrs::rev),
-// for launches that run two passes (dQ forward and dK reverse).  The reverse
-// direction needs kZS (the host checks gamma^CT >= 2^-100).
-struct PassPtrs {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  const float* state_in;  // nullable
-  float* state_out;       // nullable
-  uint16_t* y;
-  int rev;         // reverse direction (kDir = 2)
-  int state_in_t;  // state_in stored transposed, [dv x DK] per head (one segment only)
-};
+// for launches that run one or two passes of either direction (dQ forward,
+// dK and dV reverse).
 
 template <int CT, int DK, bool kOut, bool kZS, int kDir>
 __global__ __attribute__((amdgpu_flat_work_group_size(kOut ? 512 : 256, kOut ? 512 : 256),
@@ -122,7 +124,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kOut ? 512 : 256, kOut ? 5
 chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H, int h0, int nh, int Tn, int dv,
                       int C, int ntiles, SegArgs sg) {
   using F = Cfg<CT, DK>;
-  static_assert(kDir == 0 || kZS, "the reverse pass stages zeta V");
   constexpr int NSP = CT / 32;  // key (token) steps of 32 per chunk tile
   constexpr int NB = F::NBUF;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[NB][CT * F::KLD];
@@ -189,9 +190,9 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
   // [d_k x 64] tile moves through LDS (the K buffers, before the first chunk is
   // staged and after the last one is read), so that global accesses are whole
   // 256-byte rows; SRN rounds of SRR rows, two barriers per round in every wave.
-  const float* init = !kOut ? nullptr : (sg.nseg > 1 ? sg.ws + seg * sg.ws_stride : P.state_in);
+  const float* init = !kOut ? nullptr : (sg.nseg > 1 ? P.ws + seg * sg.ws_stride : P.state_in);
   const bool init_t = sg.nseg == 1 && P.state_in_t != 0;  // init is stored transposed
-  float* fin = kOut ? (seg == sg.nseg - 1 ? P.state_out : nullptr) : sg.ws + (seg + 1) * sg.ws_stride;
+  float* fin = kOut ? (seg == sg.nseg - 1 ? P.state_out : nullptr) : P.ws + (seg + 1) * sg.ws_stride;
   constexpr int SLD = kTN + 4;                 // fp32 row stride in LDS
   constexpr int SRR = DK < 128 ? DK : 128;     // rows per round
   constexpr int SRN = DK / SRR;                // rounds
@@ -315,18 +316,19 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
 #pragma unroll
       for (int r = 0; r < F::VPT; ++r) {
         const int row = prow + 32 * r;
-        const float z = row < Ln ? gamma_pow(lg, Ln - 1 - row) : 0.0f;
+        const float z = row < Ln ? gamma_pow(lg, Ln - 1 - row + kShift) : 0.0f;
         const f32x8 vf = __builtin_convertvector(__builtin_bit_cast(bf16x8, vreg[0][r]), f32x8) * z;
         *reinterpret_cast<bf16x8*>(&Vz[row * F::VLD + 8 * vc8]) = __builtin_convertvector(vf, bf16x8);
       }
     };
-    // zeta_t = gamma^(L-1-t) for the tokens t = 32s + 8g + 2(e%4) + e/4 this lane
-    // holds in the update's B operand; for chunks that fill the tile (L = CT),
-    // zeta = zbase[s] * zc[e] with zbase[s] = gamma^(CT-8-32s-8g) and
-    // zc[e] = gamma^(7-2(e%4)-e/4) (both exponents >= 0).
+    // zeta_t = gamma^(L-1-t) (gamma^(L-t) in reverse) for the tokens
+    // t = 32s + 8g + 2(e%4) + e/4 this lane holds in the update's B operand;
+    // for chunks that fill the tile (L = CT), zeta = zbase[s] * zc[e] with
+    // zbase[s] = gamma^(CT-8-32s-8g (+1)) and zc[e] = gamma^(7-2(e%4)-e/4)
+    // (both exponents >= 0).
     float zbase[NSP], zc[8];
 #pragma unroll
-    for (int s = 0; s < NSP; ++s) zbase[s] = gamma_pow(lg, CT - 8 - 32 * s - 8 * g);
+    for (int s = 0; s < NSP; ++s) zbase[s] = gamma_pow(lg, CT - 8 - 32 * s - 8 * g + kShift);
 #pragma unroll
     for (int e = 0; e < 8; ++e) zc[e] = gamma_pow(lg, 7 - 2 * (e & 3) - (e >> 2));
 
@@ -382,7 +384,7 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int t = 32 * s + 8 * g + 2 * (e & 3) + (e >> 2);
-            z[e] = t < L ? gamma_pow(lg, L - 1 - t) : 0.0f;
+            z[e] = t < L ? gamma_pow(lg, L - 1 - t + kShift) : 0.0f;
           }
         }
 #pragma unroll
@@ -690,9 +692,11 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
 
 // ws slot s <- incoming state of segment s: slot 0 = state_in (or 0), slot s =
 // gamma^seg_len * slot (s-1) + (end state of segment s-1 from zero).
+// state_in_t: state_in holds each head's [da x dx] state transposed.
 __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ ws, const float* state_in,
-                                                           HeadDecay gam, int H, int h0, int nh, int B, long per_head,
-                                                           int nseg, int seg_len, long stride) {
+                                                           int state_in_t, int dx, HeadDecay gam, int H, int h0,
+                                                           int nh, int B, long per_head, int nseg, int seg_len,
+                                                           long stride) {
   const long n = static_cast<long>(B) * nh * per_head;
   for (long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x; idx < n;
        idx += static_cast<long>(gridDim.x) * blockDim.x) {
@@ -702,7 +706,8 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ w
     const long head = (bh / nh) * H + h0 + hl;
     const long off = head * per_head + within;
     const float gs = gamma_pow(gam.log2g[hl], seg_len);
-    float s = state_in != nullptr ? state_in[off] : 0.0f;
+    const long src = state_in_t ? head * per_head + (within % dx) * (per_head / dx) + within / dx : off;
+    float s = state_in != nullptr ? state_in[src] : 0.0f;
     ws[off] = s;
     for (int sg = 1; sg < nseg; ++sg) {
       s = fmaf(gs, s, ws[sg * stride + off]);
@@ -711,56 +716,63 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ w
   }
 }
 
+// One launch sequence of the kernel: with segments, the state-only launch over
+// segments 0..nseg-2, the scan of every pass, then the full launch.
 template <int CT, int DK, bool kZS, int kDir>
-hipError_t launch_cfg(const void* q, const void* k, const void* v, const float* state_in, float* state_out, void* y,
-                      int B, int H, int Tn, int dv, int C, const HeadDecay& hd, const HeadGroup& g,
-                      const ChunkSegments& segs, float* ws, hipStream_t s) {
-  const int ntiles = dv / kTN;
-  const int bnh = B * g.nh;
-  SegArgs sg{segs.seg_len, segs.nseg, bnh, ws, static_cast<long>(B) * H * DK * dv};
-  const PassPtrs pp{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                    state_in, state_out, static_cast<uint16_t*>(y), kDir == 1, 0};
-  if (segs.nseg > 1) {
-    // end states of segments 0..nseg-2 from zero, then the scan over segments
-    hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, false, kZS, kDir>), dim3(bnh * ntiles * (segs.nseg - 1)), dim3(256),
-                       0, s, pp, pp, 1, hd, H, g.h0, g.nh, Tn, dv, C, ntiles, sg);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const long per_head = static_cast<long>(DK) * dv;
-    const long n = static_cast<long>(bnh) * per_head;
-    const unsigned blocks = static_cast<unsigned>(min(65536L, (n + 255) / 256));
-    hipLaunchKernelGGL(segment_scan_kernel, dim3(blocks), dim3(256), 0, s, ws, state_in, hd, H, g.h0, g.nh, B,
-                       per_head, segs.nseg, segs.seg_len, sg.ws_stride);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, true, kZS, kDir>), dim3(bnh * ntiles * segs.nseg), dim3(512), 0, s, pp,
-                     pp, 1, hd, H, g.h0, g.nh, Tn, dv, C, ntiles, sg);
-  return hipGetLastError();
-}
-
-template <int CT, bool kZS, int kDir = 0>
-hipError_t launch_ct(const void* q, const void* k, const void* v, const float* state_in, float* state_out, void* y,
-                     int B, int H, int Tn, int dk, int dv, int C, const HeadDecay& hd, const HeadGroup& g,
-                     const ChunkSegments& segs, float* ws, hipStream_t s) {
-  switch (dk) {
-    case 64: return launch_cfg<CT, 64, kZS, kDir>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
-    case 128: return launch_cfg<CT, 128, kZS, kDir>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
-    default: return launch_cfg<CT, 256, kZS, kDir>(q, k, v, state_in, state_out, y, B, H, Tn, dv, C, hd, g, segs, ws, s);
-  }
-}
-
-// Two passes of one d_a (= DK) and X width in one launch, one segment: the
-// column tiles of both passes of a head are adjacent work items (one XCD).
-template <int DK>
-hipError_t launch_pair_dk(const PassPtrs& a, const PassPtrs& b, int B, int H, int Tn, int dx, const HeadDecay& hd,
-                          const HeadGroup& g, hipStream_t s) {
+hipError_t launch_cfg(const PassPtrs (&pp)[2], int npass, int B, int H, int Tn, int dx, int C, const HeadDecay& hd,
+                      const HeadGroup& g, const ChunkSegments& segs, hipStream_t s) {
   const int ntiles = dx / kTN;
   const int bnh = B * g.nh;
-  const SegArgs sg{Tn, 1, bnh, nullptr, 0};
-  hipLaunchKernelGGL((chunkwise_mfma_kernel<kRevChunk, DK, true, true, 2>), dim3(bnh * ntiles * 2), dim3(512), 0, s, a,
-                     b, 2, hd, H, g.h0, g.nh, Tn, dx, kRevChunk, ntiles, sg);
+  const SegArgs sg{segs.seg_len, segs.nseg, bnh, static_cast<long>(B) * H * DK * dx};
+  const int items = bnh * ntiles * npass;
+  if (segs.nseg > 1) {
+    hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, false, kZS, kDir>), dim3(items * (segs.nseg - 1)), dim3(256), 0,
+                       s, pp[0], pp[1], npass, hd, H, g.h0, g.nh, Tn, dx, C, ntiles, sg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long per_head = static_cast<long>(DK) * dx;
+    const long n = static_cast<long>(bnh) * per_head;
+    const unsigned blocks = static_cast<unsigned>(min(65536L, (n + 255) / 256));
+    for (int i = 0; i < npass; ++i) {
+      hipLaunchKernelGGL(segment_scan_kernel, dim3(blocks), dim3(256), 0, s, pp[i].ws, pp[i].state_in,
+                         pp[i].state_in_t, dx, hd, H, g.h0, g.nh, B, per_head, segs.nseg, segs.seg_len, sg.ws_stride);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, true, kZS, kDir>), dim3(items * segs.nseg), dim3(512), 0, s, pp[0],
+                     pp[1], npass, hd, H, g.h0, g.nh, Tn, dx, C, ntiles, sg);
   return hipGetLastError();
+}
+
+template <int CT, bool kZS>
+hipError_t launch_fwd_ct(const PassPtrs (&pp)[2], int B, int H, int Tn, int dk, int dv, int C, const HeadDecay& hd,
+                         const HeadGroup& g, const ChunkSegments& segs, hipStream_t s) {
+  switch (dk) {
+    case 64: return launch_cfg<CT, 64, kZS, 0>(pp, 1, B, H, Tn, dv, C, hd, g, segs, s);
+    case 128: return launch_cfg<CT, 128, kZS, 0>(pp, 1, B, H, Tn, dv, C, hd, g, segs, s);
+    default: return launch_cfg<CT, 256, kZS, 0>(pp, 1, B, H, Tn, dv, C, hd, g, segs, s);
+  }
+}
+
+template <bool kZS>
+hipError_t launch_passes_zs(const PassPtrs (&pp)[2], int npass, int B, int H, int Tn, int da, int dx,
+                            const HeadDecay& hd, const HeadGroup& g, const ChunkSegments& segs, hipStream_t s) {
+  constexpr int C = kPassChunk;
+  switch (da) {
+    case 64: return launch_cfg<C, 64, kZS, 2>(pp, npass, B, H, Tn, dx, C, hd, g, segs, s);
+    case 128: return launch_cfg<C, 128, kZS, 2>(pp, npass, B, H, Tn, dx, C, hd, g, segs, s);
+    case 256: return launch_cfg<C, 256, kZS, 2>(pp, npass, B, H, Tn, dx, C, hd, g, segs, s);
+    default: return launch_cfg<C, 512, kZS, 2>(pp, npass, B, H, Tn, dx, C, hd, g, segs, s);
+  }
+}
+
+// zeta-staged V when every head's zeta and gamma^(-L) stay within 2^+-100:
+// gamma^e >= 2^-100 for the largest zeta exponent e
+bool zeta_staged(const HeadDecay& hd, int nh, int e) {
+  bool zs = true;
+  for (int i = 0; i < nh; ++i) zs = zs && static_cast<double>(e) * hd.log2g[i] >= -100.0;
+  return zs;
 }
 
 }  // namespace
@@ -792,57 +804,36 @@ hipError_t launch_chunkwise_mfma(const void* q, const void* k, const void* v, co
                                  float* state_out, void* y, int B, int H, int T, int dk, int dv, int C,
                                  const ChunkSegments& segs, float* ws, const HeadGroup& g, hipStream_t s) {
   const HeadDecay hd = make_head_decay(g);
-  // zeta-staged V when gamma^(CT-1) >= 2^-100 for every head of the group
+  const PassPtrs p{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                   state_in, state_out, static_cast<uint16_t*>(y), 0, 0, ws};
+  const PassPtrs pp[2] = {p, p};
   const int ct = C <= 64 ? 64 : 128;
-  bool zs = true;
-  for (int i = 0; i < g.nh; ++i) zs = zs && static_cast<double>(ct - 1) * hd.log2g[i] >= -100.0;
+  const bool zs = zeta_staged(hd, g.nh, ct - 1);
   if (C <= 64) {
-    if (zs) return launch_ct<64, true>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, hd, g, segs, ws, s);
-    return launch_ct<64, false>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, hd, g, segs, ws, s);
+    if (zs) return launch_fwd_ct<64, true>(pp, B, H, T, dk, dv, C, hd, g, segs, s);
+    return launch_fwd_ct<64, false>(pp, B, H, T, dk, dv, C, hd, g, segs, s);
   }
-  if (zs) return launch_ct<128, true>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, hd, g, segs, ws, s);
-  return launch_ct<128, false>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, hd, g, segs, ws, s);
+  if (zs) return launch_fwd_ct<128, true>(pp, B, H, T, dk, dv, C, hd, g, segs, s);
+  return launch_fwd_ct<128, false>(pp, B, H, T, dk, dv, C, hd, g, segs, s);
 }
 
-bool chunkwise_mfma_rev_supports(int dk, int dv, const HeadGroup& g) {
-  if (!chunkwise_mfma_supports(0, dk, dv, kRevChunk, 1)) return false;
-  const HeadDecay hd = make_head_decay(g);
-  for (int i = 0; i < g.nh; ++i)
-    if (!(static_cast<double>(kRevChunk) * hd.log2g[i] >= -100.0)) return false;  // zeta = gamma^(L-t) >= gamma^CT
-  return true;
+bool chunkwise_mfma_pass_supports(int da, int dx) {
+  return (da == 64 || da == 128 || da == 256 || da == 512) && dx % kTN == 0;
 }
 
-bool chunkwise_mfma_pair_supports(int da, int dx, const HeadGroup& g) {
-  if (!(da == 64 || da == 128 || da == 256 || da == 512) || dx % kTN != 0) return false;
+hipError_t launch_chunkwise_mfma_passes(const ChunkPass* p, int npass, int B, int H, int T, int da, int dx,
+                                        const ChunkSegments& segs, const HeadGroup& g, hipStream_t s) {
   const HeadDecay hd = make_head_decay(g);
-  for (int i = 0; i < g.nh; ++i)
-    if (!(static_cast<double>(kRevChunk) * hd.log2g[i] >= -100.0)) return false;
-  return true;
-}
-
-hipError_t launch_chunkwise_mfma_pair(const ChunkPass& a, const ChunkPass& b, int B, int H, int T, int da, int dx,
-                                      const HeadGroup& g, hipStream_t s) {
-  const HeadDecay hd = make_head_decay(g);
-  auto pp = [](const ChunkPass& c) {
-    return PassPtrs{static_cast<const uint16_t*>(c.q), static_cast<const uint16_t*>(c.k),
-                    static_cast<const uint16_t*>(c.v), c.state_in, c.state_out, static_cast<uint16_t*>(c.y), c.rev,
-                    c.state_in_t};
-  };
-  const PassPtrs pa = pp(a), pb = pp(b);
-  switch (da) {
-    case 64: return launch_pair_dk<64>(pa, pb, B, H, T, dx, hd, g, s);
-    case 128: return launch_pair_dk<128>(pa, pb, B, H, T, dx, hd, g, s);
-    case 256: return launch_pair_dk<256>(pa, pb, B, H, T, dx, hd, g, s);
-    default: return launch_pair_dk<512>(pa, pb, B, H, T, dx, hd, g, s);
+  PassPtrs pp[2];
+  for (int i = 0; i < 2; ++i) {
+    const ChunkPass& c = p[i < npass ? i : 0];
+    pp[i] = PassPtrs{static_cast<const uint16_t*>(c.q), static_cast<const uint16_t*>(c.k),
+                     static_cast<const uint16_t*>(c.v), c.state_in, c.state_out, static_cast<uint16_t*>(c.y), c.rev,
+                     c.state_in_t, c.ws};
   }
-}
-
-hipError_t launch_chunkwise_mfma_rev(const void* q, const void* k, const void* v, const float* state_in,
-                                     float* state_out, void* y, int B, int H, int T, int dk, int dv,
-                                     const ChunkSegments& segs, float* ws, const HeadGroup& g, hipStream_t s) {
-  const HeadDecay hd = make_head_decay(g);
-  return launch_ct<kRevChunk, true, 1>(q, k, v, state_in, state_out, y, B, H, T, dk, dv, kRevChunk, hd, g, segs,
-                                          ws, s);
+  // reverse passes weight by up to gamma^C: the stricter bound for both directions
+  if (zeta_staged(hd, g.nh, kPassChunk)) return launch_passes_zs<true>(pp, npass, B, H, T, da, dx, hd, g, segs, s);
+  return launch_passes_zs<false>(pp, npass, B, H, T, da, dx, hd, g, segs, s);
 }
 
 }  // namespace ret

@@ -49,25 +49,20 @@ hipError_t launch_chunkwise_mfma(const void* q, const void* k, const void* v, co
                                  float* state_out, void* y, int B, int H, int T, int dk, int dv, int C,
                                  const ChunkSegments& segs, float* ws, const HeadGroup& g, hipStream_t s);
 
-// The same kernel backwards in time with the decay weights of the value
-// gradient: for position p = Tn-1-n (n the token) and chunk rows j,
+// Passes of the same kernel for the gradients, in chunks of kPassChunk
+// positions: each pass runs forward in time or backwards with the decay
+// weights shifted by one token (rev = 1; position p = T-1-n for token n, chunk
+// rows j):
 //   Y_j = gamma^j Q_j R + sum_{t<=j} gamma^(j-t) (Q_j . K_t) V_t,
-//   R <- gamma^L R + sum_t gamma^(L-t) K_t^T V_t,
-// in chunks of kRevChunk positions.  With (Q, K, V, R_0) = (K, Q, dY, dS_out)
-// it writes dV and its final state is dS_in.  Segments as for the forward
-// (chunkwise_mfma_segments with C = kRevChunk).  Needs gamma^kRevChunk >=
-// 2^-100 for every head (chunkwise_mfma_rev_supports).
-constexpr int kRevChunk = 64;
-bool chunkwise_mfma_rev_supports(int dk, int dv, const HeadGroup& g);
-hipError_t launch_chunkwise_mfma_rev(const void* q, const void* k, const void* v, const float* state_in,
-                                     float* state_out, void* y, int B, int H, int T, int dk, int dv,
-                                     const ChunkSegments& segs, float* ws, const HeadGroup& g, hipStream_t s);
-
-// Two passes of that kernel in one launch (one segment, chunks of kRevChunk,
-// T >= 1): each pass forward or reverse in time, its initial state optionally
-// stored transposed ([dx, da] per head), bf16 inputs, d_a in {64, 128, 256,
-// 512}, dx % 64 == 0.  dQ (forward over dY, V, K from S_in^T) and dK (reverse
-// over V, dY, Q from dS_out^T) take it.
+//   R <- gamma^L R + sum_t gamma^(L-t) K_t^T V_t.
+// One launch runs one or two passes of one d_a (Q and K width, in {64, 128,
+// 256, 512}) and X width dx (V and Y, a multiple of 64), bf16, T >= 1.  The
+// initial state may be stored transposed ([dx, da] per head).  With
+// segments (segs.nseg > 1, seg_len a multiple of kPassChunk) each pass needs
+// ws: nseg slots of B*H*da*dx fp32.
+//   dQ: forward over (dY, V, K) from S_in^T;  dK: reverse over (V, dY, Q)
+//   from dS_out^T;  dV: reverse over (K, Q, dY) from dS_out, final state dS_in.
+constexpr int kPassChunk = 64;
 struct ChunkPass {
   const void* q;
   const void* k;
@@ -77,10 +72,11 @@ struct ChunkPass {
   int rev;
   float* state_out;  // nullable
   void* y;
+  float* ws;  // segment slots (segmented launches)
 };
-bool chunkwise_mfma_pair_supports(int da, int dx, const HeadGroup& g);
-hipError_t launch_chunkwise_mfma_pair(const ChunkPass& a, const ChunkPass& b, int B, int H, int T, int da, int dx,
-                                      const HeadGroup& g, hipStream_t s);
+bool chunkwise_mfma_pass_supports(int da, int dx);
+hipError_t launch_chunkwise_mfma_passes(const ChunkPass* p, int npass, int B, int H, int T, int da, int dx,
+                                        const ChunkSegments& segs, const HeadGroup& g, hipStream_t s);
 
 // Streaming chunkwise kernel for a short block of tokens from a carried state
 // (1 <= T <= kShortChunkMaxT, fp32 or bf16 inputs, any supported dk and dv):
@@ -107,7 +103,8 @@ struct BwdArgs {
 bool chunkwise_bwd_generic_supports(int dk, int dv);
 hipError_t launch_chunkwise_bwd_generic(const BwdArgs& a, int B, int H, int T, int dk, int dv, int dt,
                                         const HeadGroup& g, hipStream_t s);
-// bf16 MFMA passes: bf16 inputs with dk, dv in {64, 128, 256, 512}.
+// bf16 MFMA passes (the chunkwise kernel's gradient passes): bf16 inputs with
+// dk, dv in {64, 128, 256, 512}.
 bool chunkwise_bwd_mfma_supports(int dk, int dv, int dt);
 // Sequence segments of a backward call on the MFMA passes, and the fp32
 // workspace they need (0: none); pure functions of the sizes.

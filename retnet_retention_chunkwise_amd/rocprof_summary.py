@@ -2,12 +2,13 @@
 
     python -m retnet_retention_chunkwise_amd.rocprof_summary stats <kernel_stats.csv> [--cmd "..."]
     python -m retnet_retention_chunkwise_amd.rocprof_summary traffic --fetch <dir> --write <dir> \
-        --kernel <name substring>[,<substring>...] --source <kernel .hip> --copy-mib <N> [--cmd "..."]
+        --kernel '<name substring>[|<substring>...]' --source <kernel .hip> --copy-mib <N> [--cmd "..."]
 
 `stats` turns a `--kernel-trace --stats` kernel_stats.csv into a short text
 table.  `traffic` turns two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs into
 HBM bytes per launch of one kernel (or per call of several kernels, one
-dispatch of each, given as comma-separated name substrings), calibrated against a plain copy of
+dispatch of each, given as name substrings separated by '|', since template
+argument lists hold commas), calibrated against a plain copy of
 `--copy-mib` MiB measured in the same runs (bytes = counter * known copy bytes /
 copy's counter), and records the sha256 of the kernel source so that a reader
 can tell whether the figures still describe the current kernel.
@@ -66,8 +67,8 @@ def _mean_for(entries, substr):
 def traffic(fetch_dir, write_dir, kernel, source, copy_mib, copy_substr="copy", cmd=""):
     f_entries = _per_dispatch(fetch_dir, "FETCH_SIZE")
     w_entries = _per_dispatch(write_dir, "WRITE_SIZE")
-    # a call made of several kernels (comma-separated substrings): one dispatch of each
-    parts = [k for k in kernel.split(",") if k]
+    # a call made of several kernels ('|'-separated substrings): one dispatch of each
+    parts = [k for k in kernel.split("|") if k]
     k_fetch = k_write = 0.0
     n_f, n_w = [], []
     for part in parts:

@@ -187,6 +187,9 @@ BWD_CASES = [
     (2, 2, 257, 256, 512, 128, "bf16", False, False, [0.999, 0.8]),
     (1, 2, 1, 256, 256, 1, "bf16", True, True, [0.9, 0.6]),
     (1, 130, 40, 64, 64, 32, "bf16", True, True, None),
+    # a small gamma (gamma^64 < 2^-100): V kept unscaled, zeta applied in
+    # registers, in both directions and at d_a = 512
+    (1, 2, 150, 256, 512, 64, "bf16", True, True, [0.2, 0.9]),
     # few walkers over long sequences: sequence segments (state-only launch,
     # scan over segments in each pass's direction, full launch), incl. a short
     # last segment and gamma = 1
@@ -194,6 +197,7 @@ BWD_CASES = [
     (1, 2, 3001, 128, 256, 64, "bf16", True, True, [0.995, 0.9]),
     (1, 1, 2500, 256, 512, 128, "bf16", False, False, [1.0]),
     (1, 130, 1024, 64, 64, 64, "bf16", True, True, None),
+    (1, 1, 2048, 128, 128, 64, "bf16", True, True, [0.3]),
 ]
 
 
