@@ -106,8 +106,10 @@ ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, 
  * chosen kernel needs none).  bf16 calls whose (batch, head, 64-column tile)
  * count is below the device's 256 compute units and whose sequence has at
  * least 16 chunks run in sequence segments; they need one fp32 state slot per
- * segment: nseg * B * H * dk * dv * 4 bytes.  A pure function of the sizes.
- * Returns (size_t)-1 for arguments the call would reject. */
+ * segment and per sub-segment of the pass that finds the segments' incoming
+ * states: (nseg + nsub * (nseg - 1)) * B * H * dk * dv * 4 bytes.  A pure
+ * function of the sizes.  Returns (size_t)-1 for arguments the call would
+ * reject. */
 size_t retention_chunkwise_workspace_bytes(int B, int H, int T, int dk, int dv, int C, ret_dtype dt);
 
 /*
@@ -150,8 +152,9 @@ ret_status retention_chunkwise_bwd(const void* q, const void* k, const void* v, 
  * call needs none: fp32 inputs, or enough (batch, head, column) walkers to fill
  * the device).  Few heads over a long sequence are split into sequence
  * segments whose incoming states are found by a scan; the workspace holds one
- * fp32 state per segment and pass: 3 * nseg * B*H*dk*dv * 4 bytes.  Returns
- * (size_t)-1 for arguments the call would reject. */
+ * fp32 state per segment and sub-segment and pass:
+ * 3 * (nseg + nsub * (nseg - 1)) * B*H*dk*dv * 4 bytes.  Returns (size_t)-1
+ * for arguments the call would reject. */
 size_t retention_chunkwise_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C, ret_dtype dt);
 
 /*

@@ -146,8 +146,7 @@ size_t retention_chunkwise_workspace_bytes(int B, int H, int T, int dk, int dv, 
   if (T <= ret::kShortChunkMaxT || !ret::chunkwise_mfma_supports(T, dk, dv, C, static_cast<int>(dt))) return 0;
   if (T <= ret::kShortMfmaMaxT && T >= ret::kShortMfmaMinT && ret::short_mfma_supports(T, dk, dv)) return 0;
   const ret::ChunkSegments segs = ret::chunkwise_mfma_segments(B, H, T, dv, C);
-  if (segs.nseg <= 1) return 0;
-  return static_cast<size_t>(segs.nseg) * B * H * dk * dv * sizeof(float);
+  return ret::chunkwise_segment_slots(segs) * B * H * dk * dv * sizeof(float);
 }
 
 ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, const float* gamma,
@@ -208,7 +207,7 @@ ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, 
   }
   const bool mfma = ret::chunkwise_mfma_supports(T, dk, dv, C, static_cast<int>(dt));
   const bool f32 = ret::chunkwise_f32_mfma_supports(dk, dv, static_cast<int>(dt));
-  const ret::ChunkSegments segs = mfma ? ret::chunkwise_mfma_segments(B, H, T, dv, C) : ret::ChunkSegments{T, 1};
+  const ret::ChunkSegments segs = mfma ? ret::chunkwise_mfma_segments(B, H, T, dv, C) : ret::ChunkSegments{T, 1, 1};
   float* ws = static_cast<float*>(workspace);
   return for_head_groups(fn, H, gamma, [&](const ret::HeadGroup& g) {
     if (mfma) return ret::launch_chunkwise_mfma(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, segs, ws, g, s);

@@ -30,11 +30,12 @@ bool chunkwise_bwd_mfma_supports(int dk, int dv, int dt) { return dt == 1 && da_
 
 // Few walkers in the smaller launch over a long sequence: segments of at least
 // kMinSegChunks chunks of kPassChunk positions, so that the smaller launch
-// fills about kTargetWorkgroups workgroups.  A pure function of the sizes.
+// fills about kTargetWorkgroups workgroups, and sub-segments for the
+// state-only launches.  A pure function of the sizes.
 ChunkSegments chunkwise_bwd_segments(int B, int H, int T, int dk, int dv) {
   constexpr long kTargetWorkgroups = 256;  // MI355X compute units
   constexpr int kMinSegChunks = 8;
-  ChunkSegments r{T > 0 ? T : 1, 1};
+  ChunkSegments r{T > 0 ? T : 1, 1, 1};
   const long walkers = static_cast<long>(B) * H * std::min(2 * (dk / 64), dv / 64);
   const long nchunks = (static_cast<long>(T) + kPassChunk - 1) / kPassChunk;
   if (walkers < 1 || walkers >= kTargetWorkgroups || nchunks < 2 * kMinSegChunks) return r;
@@ -44,22 +45,23 @@ ChunkSegments chunkwise_bwd_segments(int B, int H, int T, int dk, int dv) {
   const long per = (nchunks + want - 1) / want;  // chunks per segment
   r.seg_len = static_cast<int>(per * kPassChunk);
   r.nseg = static_cast<int>((nchunks + per - 1) / per);
+  r.nsub = state_pass_split(walkers, r.nseg, r.seg_len);
   return r;
 }
 
 size_t chunkwise_bwd_workspace_floats(int B, int H, int T, int dk, int dv) {
   const ChunkSegments sg = chunkwise_bwd_segments(B, H, T, dk, dv);
-  if (sg.nseg <= 1) return 0;
-  return static_cast<size_t>(3) * sg.nseg * B * H * dk * dv;  // dV, dK and dQ slots
+  return 3 * chunkwise_segment_slots(sg) * B * H * dk * dv;  // dV, dK and dQ slots
 }
 
 hipError_t launch_chunkwise_bwd_mfma(const BwdArgs& a, int B, int H, int T, int dk, int dv, float* ws,
                                      const HeadGroup& g, hipStream_t s) {
   const ChunkSegments sg = chunkwise_bwd_segments(B, H, T, dk, dv);
   const long slot = static_cast<long>(B) * H * dk * dv;
+  const long per_pass = static_cast<long>(chunkwise_segment_slots(sg)) * slot;
   float* wv = sg.nseg > 1 ? ws : nullptr;
-  float* wk = sg.nseg > 1 ? ws + sg.nseg * slot : nullptr;
-  float* wq = sg.nseg > 1 ? ws + 2 * sg.nseg * slot : nullptr;
+  float* wk = sg.nseg > 1 ? ws + per_pass : nullptr;
+  float* wq = sg.nseg > 1 ? ws + 2 * per_pass : nullptr;
   const ChunkPass kq[2] = {
       {a.v, a.dy, a.q, a.dstate_out, 1, 1, nullptr, a.dk, wk},  // dK
       {a.dy, a.v, a.k, a.state_in, 1, 0, nullptr, a.dq, wq},    // dQ

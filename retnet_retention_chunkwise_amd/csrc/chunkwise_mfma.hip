@@ -49,7 +49,7 @@ namespace {
 
 constexpr int kTN = 64;  // value columns per workgroup
 
-template <int CT, int DK>
+template <int CT, int DK, bool kOut>
 struct Cfg {
   static constexpr int kThreads = 512;         // 4 output waves + 4 state waves
   static constexpr int kStageThreads = 256;    // the state waves stage K/V
@@ -63,8 +63,10 @@ struct Cfg {
   static constexpr int VPT = CT * kTN / 8 / kStageThreads;  // 16-byte V pieces per staging thread
   // 64-token tiles fit two copies of K, V and R^T in LDS: the state waves then
   // stage chunk i+1 while the output waves work on chunk i (one barrier per
-  // chunk).  128-token tiles keep one copy and two barriers per chunk.
-  static constexpr int NBUF = (2 * (CT * KLD + CT * VLD + kTN * RLD) * 2 <= 160 * 1024) ? 2 : 1;
+  // chunk).  128-token tiles keep one copy and two barriers per chunk.  The
+  // state-only pass keeps one copy of K and V and no R^T (43 KB at d_k = 256
+  // and 64-token tiles), so that several of its workgroups share a CU.
+  static constexpr int NBUF = kOut && (2 * (CT * KLD + CT * VLD + kTN * RLD) * 2 <= 160 * 1024) ? 2 : 1;
   static_assert(NQ >= 1 && NQ <= 2 && RM >= 1, "unsupported tile");
   static_assert(KPT >= 1 && VPT >= 1, "tile too small for the staging split");
 };
@@ -123,12 +125,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kOut ? 512 : 256, kOut ? 5
                           amdgpu_waves_per_eu(kOut ? 2 : 1, 2))) void
 chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H, int h0, int nh, int Tn, int dv,
                       int C, int ntiles, SegArgs sg) {
-  using F = Cfg<CT, DK>;
+  using F = Cfg<CT, DK, kOut>;
   constexpr int NSP = CT / 32;  // key (token) steps of 32 per chunk tile
   constexpr int NB = F::NBUF;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[NB][CT * F::KLD];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[NB][CT * F::VLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Rt[NB][kTN * F::RLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Rt[NB][kOut ? kTN * F::RLD : 8];
   // With one LDS copy there is room for zeta*V, formed once when V is staged;
   // with two copies zeta is applied to the update's V operand in registers.
   constexpr bool kVz = NB == 1 && !kZS;
@@ -194,7 +196,10 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
   const bool init_t = sg.nseg == 1 && P.state_in_t != 0;  // init is stored transposed
   float* fin = kOut ? (seg == sg.nseg - 1 ? P.state_out : nullptr) : P.ws + (seg + 1) * sg.ws_stride;
   constexpr int SLD = kTN + 4;                 // fp32 row stride in LDS
-  constexpr int SRR = DK < 128 ? DK : 128;     // rows per round
+  constexpr int kKBytes = NB * CT * F::KLD * 2;  // bytes of the K buffers
+  constexpr int SRR = (DK >= 128 && 128 * SLD * 4 <= kKBytes) ? 128
+                      : (DK >= 64 && 64 * SLD * 4 <= kKBytes) ? 64
+                      : (32 * SLD * 4 <= kKBytes ? 32 : 16);  // rows per round
   constexpr int SRN = DK / SRR;                // rounds
   static_assert(SRR * SLD * 4 <= NB * CT * F::KLD * 2, "state staging does not fit the K buffers");
   float* const Sst = reinterpret_cast<float*>(&Ks[0][0]);
@@ -690,14 +695,18 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
   }
 }
 
-// ws slot s <- incoming state of segment s: slot 0 = state_in (or 0), slot s =
-// gamma^seg_len * slot (s-1) + (end state of segment s-1 from zero).
-// state_in_t: state_in holds each head's [da x dx] state transposed.
+// Incoming state of every segment.  ws: main slots 0..nseg-1, then the
+// sub-segment slots (nsub per segment of all but the last, in order), each
+// holding that sub-segment's end state from zero.  Main slot 0 = state_in (or
+// 0); main slot m = the state after segments 0..m-1, composed sub-segment by
+// sub-segment: S <- gamma^sub_len S + local.  state_in_t: state_in holds each
+// head's [da x dx] state transposed.
 __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ ws, const float* state_in,
                                                            int state_in_t, int dx, HeadDecay gam, int H, int h0,
-                                                           int nh, int B, long per_head, int nseg, int seg_len,
-                                                           long stride) {
+                                                           int nh, int B, long per_head, int nseg, int nsub,
+                                                           int sub_len, long stride) {
   const long n = static_cast<long>(B) * nh * per_head;
+  const float* sub = ws + nseg * stride;
   for (long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x; idx < n;
        idx += static_cast<long>(gridDim.x) * blockDim.x) {
     const long bh = idx / per_head;
@@ -705,29 +714,44 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ w
     const int hl = static_cast<int>(bh % nh);
     const long head = (bh / nh) * H + h0 + hl;
     const long off = head * per_head + within;
-    const float gs = gamma_pow(gam.log2g[hl], seg_len);
+    const float gs = gamma_pow(gam.log2g[hl], sub_len);
     const long src = state_in_t ? head * per_head + (within % dx) * (per_head / dx) + within / dx : off;
     float s = state_in != nullptr ? state_in[src] : 0.0f;
     ws[off] = s;
-    for (int sg = 1; sg < nseg; ++sg) {
-      s = fmaf(gs, s, ws[sg * stride + off]);
-      ws[sg * stride + off] = s;
+    for (int m = 1; m < nseg; ++m) {
+      // the sub-slot loads do not depend on s: unrolled, several are in flight
+#pragma unroll 4
+      for (int j = 0; j < nsub; ++j) s = fmaf(gs, s, sub[((m - 1) * nsub + j) * stride + off]);
+      ws[m * stride + off] = s;
     }
   }
 }
 
-// One launch sequence of the kernel: with segments, the state-only launch over
-// segments 0..nseg-2, the scan of every pass, then the full launch.
+// One launch sequence of the kernel.  With segments: the state-only launch
+// over the sub-segments of segments 0..nseg-2 (64-token chunks when the
+// sub-segment length allows, else the call's own tile and chunk), the scan of
+// every pass, then the full launch.
 template <int CT, int DK, bool kZS, int kDir>
 hipError_t launch_cfg(const PassPtrs (&pp)[2], int npass, int B, int H, int Tn, int dx, int C, const HeadDecay& hd,
                       const HeadGroup& g, const ChunkSegments& segs, hipStream_t s) {
   const int ntiles = dx / kTN;
   const int bnh = B * g.nh;
-  const SegArgs sg{segs.seg_len, segs.nseg, bnh, static_cast<long>(B) * H * DK * dx};
+  const long stride = static_cast<long>(B) * H * DK * dx;
   const int items = bnh * ntiles * npass;
   if (segs.nseg > 1) {
-    hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, false, kZS, kDir>), dim3(items * (segs.nseg - 1)), dim3(256), 0,
-                       s, pp[0], pp[1], npass, hd, H, g.h0, g.nh, Tn, dx, C, ntiles, sg);
+    const int sub_len = segs.seg_len / segs.nsub;
+    const int nsubs = segs.nsub * (segs.nseg - 1);  // sub-segments before the last segment
+    // the state-only kernel writes sub-segment i's end state to "slot i + 1"
+    // of its ws, i.e. to the sub-segment slots
+    PassPtrs pre[2] = {pp[0], pp[1]};
+    for (auto& p : pre) p.ws = p.ws + (segs.nseg - 1) * stride;
+    const SegArgs sp{sub_len, nsubs + 1, bnh, stride};
+    if (sub_len % 64 == 0)
+      hipLaunchKernelGGL((chunkwise_mfma_kernel<64, DK, false, kZS, kDir>), dim3(items * nsubs), dim3(256), 0, s,
+                         pre[0], pre[1], npass, hd, H, g.h0, g.nh, Tn, dx, 64, ntiles, sp);
+    else
+      hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, false, kZS, kDir>), dim3(items * nsubs), dim3(256), 0, s,
+                         pre[0], pre[1], npass, hd, H, g.h0, g.nh, Tn, dx, C, ntiles, sp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long per_head = static_cast<long>(DK) * dx;
@@ -735,11 +759,12 @@ hipError_t launch_cfg(const PassPtrs (&pp)[2], int npass, int B, int H, int Tn, 
     const unsigned blocks = static_cast<unsigned>(min(65536L, (n + 255) / 256));
     for (int i = 0; i < npass; ++i) {
       hipLaunchKernelGGL(segment_scan_kernel, dim3(blocks), dim3(256), 0, s, pp[i].ws, pp[i].state_in,
-                         pp[i].state_in_t, dx, hd, H, g.h0, g.nh, B, per_head, segs.nseg, segs.seg_len, sg.ws_stride);
+                         pp[i].state_in_t, dx, hd, H, g.h0, g.nh, B, per_head, segs.nseg, segs.nsub, sub_len, stride);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
   }
+  const SegArgs sg{segs.seg_len, segs.nseg, bnh, stride};
   hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, true, kZS, kDir>), dim3(items * segs.nseg), dim3(512), 0, s, pp[0],
                      pp[1], npass, hd, H, g.h0, g.nh, Tn, dx, C, ntiles, sg);
   return hipGetLastError();
@@ -781,13 +806,27 @@ bool chunkwise_mfma_supports(int /*T*/, int dk, int dv, int C, int dt) {
   return dt == 1 && (dk == 64 || dk == 128 || dk == 256) && dv % kTN == 0 && C >= 1 && C <= 128;
 }
 
+// Sub-segments of the state-only launch: about kPreWorkgroups work items
+// (several of its 4-wave workgroups share a CU), each at least kMinSubChunks
+// chunks of 64 positions; 1 when the segment length is no multiple of 128.
+int state_pass_split(long items_per_sub, int nseg, int seg_len) {
+  constexpr long kPreWorkgroups = 3 * 256;
+  constexpr int kMinSubChunks = 4;
+  if (nseg <= 1 || items_per_sub < 1) return 1;
+  const long want = (kPreWorkgroups + items_per_sub * (nseg - 1) - 1) / (items_per_sub * (nseg - 1));
+  int best = 1;
+  for (int n = 2; n <= want && n <= 64; ++n)
+    if (seg_len % (n * 64) == 0 && seg_len / n >= kMinSubChunks * 64) best = n;
+  return best;
+}
+
 // A call whose (batch, head, column tile) walkers fill fewer than
 // kTargetWorkgroups compute units is split into sequence segments (each at
 // least kMinSegChunks chunks long) so that the walkers cover the device.
 ChunkSegments chunkwise_mfma_segments(int B, int H, int T, int dv, int C) {
   constexpr long kTargetWorkgroups = 256;  // MI355X compute units
   constexpr int kMinSegChunks = 8;
-  ChunkSegments r{T > 0 ? T : 1, 1};
+  ChunkSegments r{T > 0 ? T : 1, 1, 1};
   const long walkers = static_cast<long>(B) * H * (dv / kTN);
   const long nchunks = (static_cast<long>(T) + C - 1) / C;
   if (walkers < 1 || walkers >= kTargetWorkgroups || nchunks < 2 * kMinSegChunks) return r;
@@ -797,7 +836,12 @@ ChunkSegments chunkwise_mfma_segments(int B, int H, int T, int dv, int C) {
   const long per = (nchunks + want - 1) / want;  // chunks per segment
   r.seg_len = static_cast<int>(per * C);
   r.nseg = static_cast<int>((nchunks + per - 1) / per);
+  r.nsub = state_pass_split(walkers, r.nseg, r.seg_len);
   return r;
+}
+
+size_t chunkwise_segment_slots(const ChunkSegments& sg) {
+  return sg.nseg <= 1 ? 0 : static_cast<size_t>(sg.nseg) + static_cast<size_t>(sg.nsub) * (sg.nseg - 1);
 }
 
 hipError_t launch_chunkwise_mfma(const void* q, const void* k, const void* v, const float* state_in,

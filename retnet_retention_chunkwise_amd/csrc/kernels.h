@@ -38,13 +38,19 @@ hipError_t launch_chunkwise_generic(const void* q, const void* k, const void* v,
 // bf16 MFMA chunkwise kernel; chunkwise_mfma_supports() says whether it takes a shape.
 bool chunkwise_mfma_supports(int T, int dk, int dv, int C, int dt);
 // Sequence segmentation of an MFMA call: nseg segments of seg_len tokens
-// (nseg = 1: no segmentation, no workspace).  A pure function of the sizes.
+// (nseg = 1: no segmentation, no workspace); the state-only launch splits each
+// segment but the last into nsub sub-segments.  A pure function of the sizes.
 struct ChunkSegments {
   int seg_len;
   int nseg;
+  int nsub;
 };
 ChunkSegments chunkwise_mfma_segments(int B, int H, int T, int dv, int C);
-// ws: nseg * B*H*dk*dv fp32 when segs.nseg > 1 (else unused)
+// State slots of one pass: nseg + nsub * (nseg - 1) (0 when nseg = 1).
+size_t chunkwise_segment_slots(const ChunkSegments& sg);
+// Sub-segments for a state-only launch of items_per_sub work items per sub-segment.
+int state_pass_split(long items_per_sub, int nseg, int seg_len);
+// ws: chunkwise_segment_slots(segs) * B*H*dk*dv fp32 when segs.nseg > 1 (else unused)
 hipError_t launch_chunkwise_mfma(const void* q, const void* k, const void* v, const float* state_in,
                                  float* state_out, void* y, int B, int H, int T, int dk, int dv, int C,
                                  const ChunkSegments& segs, float* ws, const HeadGroup& g, hipStream_t s);

@@ -109,16 +109,20 @@ def test_workspace_query(lib):
 
 def test_workspace_for_segmented_long_sequences(lib):
     """bf16 calls with few (batch, head, 64-column) walkers over a long sequence
-    are split into sequence segments: one fp32 state slot per segment."""
-    # B1 H8 T65536 dk256 dv512 C128: 64 walkers -> 4 segments of 16384 tokens
-    assert lib.retention_chunkwise_workspace_bytes(1, 8, 65536, 256, 512, 128, 1) == 4 * 8 * 256 * 512 * 4
+    are split into sequence segments: one fp32 state slot per segment, plus one
+    per sub-segment of the state-only launch (nsub per segment but the last,
+    about 768 work items in all, each at least 4 chunks of 64 tokens)."""
+    # B1 H8 T65536 dk256 dv512 C128: 64 walkers -> 4 segments of 16384 tokens;
+    # 64 x 3 items per sub-segment -> 4 sub-segments: 4 + 4 * 3 = 16 slots
+    assert lib.retention_chunkwise_workspace_bytes(1, 8, 65536, 256, 512, 128, 1) == 16 * 8 * 256 * 512 * 4
     # 256 walkers (B4 H8 dv512) fill the device: no segments
     assert lib.retention_chunkwise_workspace_bytes(4, 8, 2048, 256, 512, 64, 1) == 0
     # short sequences (fewer than 16 chunks) and fp32 calls never segment
     assert lib.retention_chunkwise_workspace_bytes(1, 1, 15 * 64, 64, 64, 64, 1) == 0
     assert lib.retention_chunkwise_workspace_bytes(1, 1, 65536, 64, 64, 64, 0) == 0
-    # 1 walker, 32 chunks: at most T/(8 chunks) = 4 segments
-    assert lib.retention_chunkwise_workspace_bytes(1, 1, 2048, 64, 64, 64, 1) == 4 * 64 * 64 * 4
+    # 1 walker, 32 chunks: at most T/(8 chunks) = 4 segments of 512 tokens,
+    # split in 2 sub-segments of 256 (the 4-chunk minimum): 4 + 2 * 3 = 10 slots
+    assert lib.retention_chunkwise_workspace_bytes(1, 1, 2048, 64, 64, 64, 1) == 10 * 64 * 64 * 4
 
 
 def test_segmented_call_requires_workspace(lib):
@@ -272,15 +276,16 @@ def test_host_dispatch_of_every_group_norm_parity_shape_without_a_device(lib):
 
 def test_backward_workspace_for_segmented_long_sequences(lib):
     """bf16 backward calls with few (batch, head, column) walkers over a long
-    sequence are split into sequence segments: one fp32 state slot per segment
-    and pass (dV, dK, dQ)."""
-    # B1 H8 T65536 dk256 dv512: 64 walkers -> 4 segments
-    assert lib.retention_chunkwise_bwd_workspace_bytes(1, 8, 65536, 256, 512, 128, 1) == 3 * 4 * 8 * 256 * 512 * 4
+    sequence are split into sequence segments of 64-token chunks: per pass (dV,
+    dK, dQ) one fp32 state slot per segment and per sub-segment of the
+    state-only launch."""
+    # B1 H8 T65536 dk256 dv512: 64 walkers -> 4 segments, 4 sub-segments each: 16 slots
+    assert lib.retention_chunkwise_bwd_workspace_bytes(1, 8, 65536, 256, 512, 128, 1) == 3 * 16 * 8 * 256 * 512 * 4
     # the 1.3B layer (B4 H8 T2048): 256 walkers, no segments
     assert lib.retention_chunkwise_bwd_workspace_bytes(4, 8, 2048, 256, 512, 64, 1) == 0
     # fp32 inputs (generic passes) and short sequences never segment
     assert lib.retention_chunkwise_bwd_workspace_bytes(1, 1, 65536, 64, 64, 64, 0) == 0
-    assert lib.retention_chunkwise_bwd_workspace_bytes(1, 1, 15 * 32, 64, 64, 64, 1) == 0
+    assert lib.retention_chunkwise_bwd_workspace_bytes(1, 1, 15 * 64, 64, 64, 64, 1) == 0
     bad = ctypes.c_size_t(-1).value
     assert lib.retention_chunkwise_bwd_workspace_bytes(1, 1, 64, 64, 64, 0, 1) == bad
 
