@@ -97,7 +97,9 @@ struct PassPtrs {
 };
 
 // kOut = true: the full kernel (outputs and state, 4 + 4 waves).
-// kOut = false: the state-only pass over segments 0..nseg-2 (4 state waves).
+// kOut = false: the state-only pass, end states from zero of the segments (or
+// sub-segments) given by sg (4 state waves; at d_k <= 256 three of its
+// workgroups share a CU).
 // kZS = true: V is staged in LDS already scaled by zeta_t = gamma^(L-1-t), once
 // per element, and serves both the state update and the outputs.  Since
 // gamma^(j-t) V_t = gamma^(j+1) gamma^(-L) zeta_t V_t, the outputs are
@@ -122,7 +124,7 @@ struct PassPtrs {
 
 template <int CT, int DK, bool kOut, bool kZS, int kDir>
 __global__ __attribute__((amdgpu_flat_work_group_size(kOut ? 512 : 256, kOut ? 512 : 256),
-                          amdgpu_waves_per_eu(kOut ? 2 : 1, 2))) void
+                          amdgpu_waves_per_eu(kOut ? 2 : (DK <= 256 ? 3 : 1), kOut ? 2 : 4))) void
 chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H, int h0, int nh, int Tn, int dv,
                       int C, int ntiles, SegArgs sg) {
   using F = Cfg<CT, DK, kOut>;
@@ -156,7 +158,7 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
   const int seg = lin / ntiles / npass / sg.bnh;
   const PassPtrs P = pz ? p1 : p0;
   const bool rev = kDir == 2 ? P.rev != 0 : kDir == 1;
-  const int kShift = rev ? 1 : 0;  // decay exponent shift of the reverse direction
+  const int shift = rev ? 1 : 0;  // decay exponent shift of the reverse direction
   const int hl = bh % nh;
   const int b = bh / nh;
   const long head = static_cast<long>(b) * H + h0 + hl;
@@ -308,7 +310,7 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
       for (int r = 0; r < F::VPT; ++r) {
         const int row = prow + 32 * r;
         if constexpr (kZS) {
-          const float z = row < Ln ? gamma_pow(lg, Ln - 1 - row + kShift) : 0.0f;
+          const float z = row < Ln ? gamma_pow(lg, Ln - 1 - row + shift) : 0.0f;
           const f32x8 vf = __builtin_convertvector(__builtin_bit_cast(bf16x8, vreg[set][r]), f32x8) * z;
           *reinterpret_cast<bf16x8*>(&Vs[buf][row * F::VLD + 8 * vc8]) = __builtin_convertvector(vf, bf16x8);
         } else {
@@ -321,7 +323,7 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
 #pragma unroll
       for (int r = 0; r < F::VPT; ++r) {
         const int row = prow + 32 * r;
-        const float z = row < Ln ? gamma_pow(lg, Ln - 1 - row + kShift) : 0.0f;
+        const float z = row < Ln ? gamma_pow(lg, Ln - 1 - row + shift) : 0.0f;
         const f32x8 vf = __builtin_convertvector(__builtin_bit_cast(bf16x8, vreg[0][r]), f32x8) * z;
         *reinterpret_cast<bf16x8*>(&Vz[row * F::VLD + 8 * vc8]) = __builtin_convertvector(vf, bf16x8);
       }
@@ -333,7 +335,7 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
     // (both exponents >= 0).
     float zbase[NSP], zc[8];
 #pragma unroll
-    for (int s = 0; s < NSP; ++s) zbase[s] = gamma_pow(lg, CT - 8 - 32 * s - 8 * g + kShift);
+    for (int s = 0; s < NSP; ++s) zbase[s] = gamma_pow(lg, CT - 8 - 32 * s - 8 * g + shift);
 #pragma unroll
     for (int e = 0; e < 8; ++e) zc[e] = gamma_pow(lg, 7 - 2 * (e & 3) - (e >> 2));
 
@@ -389,7 +391,7 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int t = 32 * s + 8 * g + 2 * (e & 3) + (e >> 2);
-            z[e] = t < L ? gamma_pow(lg, L - 1 - t + kShift) : 0.0f;
+            z[e] = t < L ? gamma_pow(lg, L - 1 - t + shift) : 0.0f;
           }
         }
 #pragma unroll
@@ -605,7 +607,7 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
       float xi[F::NQ];
 #pragma unroll
       for (int qi = 0; qi < F::NQ; ++qi) {
-        xi[qi] = gamma_pow(lg, 16 * (qi == 0 ? W : QB1) + c16 + 1 - kShift);
+        xi[qi] = gamma_pow(lg, 16 * (qi == 0 ? W : QB1) + c16 + 1 - shift);
         if constexpr (!kZS) {
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb) O[qi][nb] *= xi[qi];
