@@ -557,6 +557,47 @@ def test_full_size_workload_sampled_heads(key):
         check(f"{key} state[b={b},h={h}]", s[sl].cpu(), s_ref, 2e-2)
 
 
+def test_full_size_long_backward():
+    """The backward of the long-context workload (B1 H8 T65536 dk256 dv512 bf16,
+    C=128), which runs in sequence segments with sub-segmented state-only
+    launches.  Against the oracle where it is cheap and exact, on sampled
+    heads: dQ of the first W tokens (it depends only on state_in and earlier
+    tokens) and dK, dV of the last W (only on later tokens and grad_state_out).
+    All four gradients at full size through a split of the sequence: the
+    backward of the second part (state_in = the forward's state at the split)
+    hands its grad_state_in to the backward of the first part as its
+    grad_state_out, and the pieces must match the one-call gradients."""
+    wl = WORKLOADS["long64k"]
+    say(f"full-size backward: {wl.description}")
+    q, k, v, s0, dy, ds = bwd_inputs(wl.B, wl.H, wl.T, wl.dk, wl.dv, wl.dtype, seed=45)
+    gs = list(wl.gammas)
+    T, W = wl.T, 512
+    qd, kd, vd, sd, dyd, dsd = to_dev(q, k, v, s0, dy, ds)
+    got = ret.chunkwise_bwd(qd, kd, vd, gs, wl.C, dyd, state_in=sd, grad_state_out=dsd)
+    torch.cuda.synchronize()
+    say("long backward done, checking sampled heads against the oracle")
+    for b, h in sampled_heads(wl.B, wl.H):
+        g = torch.tensor([gs[h]], dtype=torch.float32)
+        first = lambda t: t[b:b + 1, h:h + 1, :W]
+        last = lambda t: t[b:b + 1, h:h + 1, T - W:]
+        head = oracle.recurrent_backward(first(q), first(k), first(v), g, first(dy), s0[b:b + 1, h:h + 1], None)
+        check(f"grad_q first {W} (b{b} h{h})", first(got[0]), head[0], 2e-2)
+        tail = oracle.recurrent_backward(last(q), last(k), last(v), g, last(dy), None, ds[b:b + 1, h:h + 1])
+        check(f"grad_k last {W} (b{b} h{h})", last(got[1]), tail[1], 2e-2)
+        check(f"grad_v last {W} (b{b} h{h})", last(got[2]), tail[2], 2e-2)
+    t = T // 2 + 1000  # not a segment boundary of either part
+    part = lambda x, lo, hi: x[:, :, lo:hi].contiguous()
+    _, s_mid = ret.chunkwise_fwd(part(qd, 0, t), part(kd, 0, t), part(vd, 0, t), gs, wl.C, state_in=sd)
+    g2 = ret.chunkwise_bwd(part(qd, t, T), part(kd, t, T), part(vd, t, T), gs, wl.C, part(dyd, t, T),
+                           state_in=s_mid, grad_state_out=dsd)
+    g1 = ret.chunkwise_bwd(part(qd, 0, t), part(kd, 0, t), part(vd, 0, t), gs, wl.C, part(dyd, 0, t),
+                           state_in=sd, grad_state_out=g2[3])
+    torch.cuda.synchronize()
+    for i, name in enumerate(("grad_q", "grad_k", "grad_v")):
+        check(f"split {name}", torch.cat([g1[i], g2[i]], dim=2), got[i], 2e-2)
+    check("split grad_state_in", g1[3], got[3], 2e-2)
+
+
 def test_full_size_decode_1000_steps_sampled_heads():
     wl = WORKLOADS["decode"]
     say(f"full decode: {wl.description}")
