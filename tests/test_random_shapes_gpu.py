@@ -78,6 +78,44 @@ def test_backward_random_shape(case):
         check(name, g, r, tol(q.dtype))
 
 
+def long_cases(n, seed):
+    """bf16 MFMA shapes with few (batch, head, column-tile) walkers over long
+    sequences, so that calls run in sequence segments (state-only launch over
+    sub-segments, scan, full launch) with random segment and sub-segment
+    counts, chunk lengths and decays."""
+    rnd = random.Random(seed)
+    out = []
+    for _ in range(n):
+        dk, dv = rnd.choice([64, 128, 256]), rnd.choice([64, 128, 256, 512])
+        H, B = rnd.choice([1, 2, 3]), rnd.choice([1, 2])
+        T = rnd.randint(900, 4200)
+        C = rnd.choice([16, 32, 48, 64, 100, 128])
+        gs = [rnd.choice([0.0, 0.2, 1.0, rnd.uniform(0.5, 0.999)]) for _ in range(H)]
+        out.append((B, H, T, dk, dv, C, "bf16", rnd.random() < 0.7, rnd.random() < 0.7, gs))
+    return out
+
+
+@pytest.mark.parametrize("case", long_cases(8, 2029), ids=lambda c: "B{}H{}T{}dk{}dv{}C{}".format(*c[:6]))
+def test_segmented_random_shape(case):
+    B, H, T, dk, dv, C, dt, with_in, with_dout, gs = case
+    say(f"segmented forward + backward {case[:9]}")
+    q, k, v, s0 = make_inputs(B, H, T, dk, dv, dt, seed=74, with_state=True)
+    _, _, dy, ds = make_inputs(B, H, T, dk, dv, dt, seed=75, with_state=True)
+    s0 = s0 if with_in else None
+    ds = ds if with_dout else None
+    g64 = torch.tensor(gs, dtype=torch.float64)
+    y_ref, s_ref = oracle.recurrent(q, k, v, g64, s0)
+    ref = oracle.recurrent_backward(q, k, v, g64, dy, s0, ds)
+    dev = lambda t: None if t is None else t.to(DEV)
+    y, s = ret.chunkwise_fwd(dev(q), dev(k), dev(v), gs, C, state_in=dev(s0))
+    got = ret.chunkwise_bwd(dev(q), dev(k), dev(v), gs, C, dev(dy), state_in=dev(s0), grad_state_out=dev(ds))
+    torch.cuda.synchronize()
+    check("y", y, y_ref, tol(q.dtype))
+    check("state_out", s, s_ref, tol(q.dtype))
+    for name, g, r in zip(("grad_q", "grad_k", "grad_v", "grad_state_in"), got, ref):
+        check(name, g, r, tol(q.dtype))
+
+
 @pytest.mark.parametrize("case", cases(12, 2028), ids=lambda c: "B{}H{}T{}dv{}{}".format(c[0], c[1], c[2], c[4], c[6]))
 def test_group_norm_random_shape(case):
     B, H, T, _, dv, _, dt, affine, in_place, _ = case
