@@ -486,6 +486,36 @@ def test_deterministic_reruns():
     assert torch.equal(y1, y2) and torch.equal(s1, s2)
 
 
+def test_side_stream_matches_default_stream():
+    """Every entry point enqueued on a non-default stream (the binding passes
+    torch's current stream through the C ABI) gives the default-stream results
+    bit for bit, including a segmented call with its workspace."""
+    say("side stream")
+    B, H, T, dk, dv, C = 1, 2, 2048, 128, 256, 64  # few walkers: segmented forward and backward
+    gs = [0.99, 0.8]
+    q, k, v, s0, dy, ds = to_dev(*bwd_inputs(B, H, T, dk, dv, "bf16", seed=46))
+    q1, k1 = q[:, :, 0].contiguous(), k[:, :, 0].contiguous()
+    v1 = v[:, :, 0].contiguous()
+
+    def run():
+        y, s = ret.chunkwise_fwd(q, k, v, gs, C, state_in=s0)
+        g = ret.chunkwise_bwd(q, k, v, gs, C, dy, state_in=s0, grad_state_out=ds)
+        st = s0.clone()
+        yd = ret.recurrent_step(q1, k1, v1, gs, st)
+        n = ret.group_norm(y)
+        return (y, s, *g, st, yd, n)
+
+    ref = run()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = run()
+    side.synchronize()
+    for i, (a, b) in enumerate(zip(got, ref)):
+        assert torch.equal(a, b), i
+
+
 def test_chunkwise_in_a_captured_graph_matches_eager():
     """Launches captured in a HIP graph (as the benchmark issues them) give the
     eager result bit for bit on every replay, with eager work and
