@@ -628,6 +628,49 @@ def test_full_size_long_backward():
     check("split grad_state_in", g1[3], got[3], 2e-2)
 
 
+def test_largest_supported_tensors():
+    """The largest tensors the ABI accepts at dk 256, dv 512: B1 H63 T65536, so v,
+    y and the value gradient hold 2.11e9 elements (over 4 GB of bf16; byte
+    offsets pass 2^32).  Forward, backward and GroupNorm on the GPU; the last
+    head (largest offsets) against the oracle: y and the state in full, dQ of
+    the first W tokens and dK, dV of the last W, GroupNorm on its last rows.
+    Inputs come from a seeded generator on the GPU; the checked head is copied
+    to the host for the oracle."""
+    B, H, T, dk, dv, C, W = 1, 63, 65536, 256, 512, 64, 256
+    assert B * H * T * dv < 2 ** 31
+    say(f"largest tensors: B{B} H{H} T{T} dk{dk} dv{dv}")
+    gen = torch.Generator(device=DEV).manual_seed(47)
+    rnd = lambda d, scale: (torch.randn(B, H, T, d, device=DEV, generator=gen) * scale).to(torch.bfloat16)
+    q, k = rnd(dk, dk ** -0.5), rnd(dk, dk ** -0.5)
+    v = rnd(dv, dk ** -0.5)
+    gs = [1 - 2 ** (-5 - 8 * h / H) for h in range(H)]
+    y, s = ret.chunkwise_fwd(q, k, v, gs, C)
+    torch.cuda.synchronize()
+    h = H - 1
+    g = torch.tensor([gs[h]], dtype=torch.float32)
+    head = lambda t: t[:, h:h + 1].cpu()
+    qh, kh, vh = head(q), head(k), head(v)
+    say("largest tensors: forward done, oracle on the last head")
+    y_ref, s_ref = oracle.chunkwise(qh, kh, vh, g, C)
+    check("y (last head)", head(y), y_ref, 2e-2)
+    check("state (last head)", head(s), s_ref, 2e-2)
+    out = ret.group_norm(y)
+    torch.cuda.synchronize()
+    check("group norm (last head, last rows)", head(out)[:, :, -W:], oracle.group_norm(head(y)[:, :, -W:], None, None,
+                                                                                      1e-5), 2e-2)
+    del out, s
+    dy = rnd(dv, 1.0)
+    got = ret.chunkwise_bwd(q, k, v, gs, C, dy, grad_state_in=False)
+    torch.cuda.synchronize()
+    say("largest tensors: backward done")
+    dyh = head(dy)
+    first = oracle.recurrent_backward(qh[:, :, :W], kh[:, :, :W], vh[:, :, :W], g, dyh[:, :, :W])
+    check("grad_q first tokens (last head)", head(got[0])[:, :, :W], first[0], 2e-2)
+    last = oracle.recurrent_backward(qh[:, :, -W:], kh[:, :, -W:], vh[:, :, -W:], g, dyh[:, :, -W:])
+    check("grad_k last tokens (last head)", head(got[1])[:, :, -W:], last[1], 2e-2)
+    check("grad_v last tokens (last head)", head(got[2])[:, :, -W:], last[2], 2e-2)
+
+
 def test_full_size_decode_1000_steps_sampled_heads():
     wl = WORKLOADS["decode"]
     say(f"full decode: {wl.description}")
