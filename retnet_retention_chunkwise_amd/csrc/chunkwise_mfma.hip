@@ -822,8 +822,9 @@ bool chunkwise_mfma_supports(int /*T*/, int dk, int dv, int C, int dt) {
 }
 
 // Sub-segments of the state-only launch: about kPreWorkgroups work items
-// (several of its 4-wave workgroups share a CU), each at least kMinSubChunks
-// chunks of 64 positions; 1 when the segment length is no multiple of 128.
+// (several of its 4-wave workgroups share a CU), each sub-segment a multiple
+// of 64 positions and at least kMinSubChunks chunks of 64; 1 when the segment
+// length allows no such split.
 int state_pass_split(long items_per_sub, int nseg, int seg_len) {
   constexpr long kPreWorkgroups = 3 * 256;
   constexpr int kMinSubChunks = 4;
