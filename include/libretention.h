@@ -90,12 +90,16 @@ ret_status retention_parallel_fwd(const void* q, const void* k, const void* v, c
  *               its contents on entry are ignored and on return undefined.  A
  *               missing or short workspace is RET_ERR_INVALID_ARG.
  * T = 0 is valid: y is untouched and state_out receives state_in (or zeros).
- * The result does not depend on C beyond rounding.  Kernels: bf16 inputs with
- * dk in {64,128,256} and dv % 64 == 0 run on bf16 MFMA with chunks of C; fp32
- * inputs with dk, dv in {64,128,256,512} run on fp32 MFMA with 16-token
- * chunks; blocks of T <= 16 tokens run as one chunk in a single streaming pass
- * over the state; every other case runs on fp32 VALU arithmetic with chunks of
- * C.  State and accumulators are fp32 throughout.
+ * The result does not depend on C beyond rounding.  Kernels, in the order the
+ * call picks them: T = 1 with state_out == state_in runs the recurrent step;
+ * blocks of 1 <= T <= 32 tokens with dk % 16 == 0 and dv % 64 == 0 (either
+ * dtype) run as one chunk in a single streaming pass over the state on fp32
+ * MFMA; other blocks of T <= 16 tokens run the same way on fp32 VALU
+ * arithmetic; bf16 inputs with dk in {64,128,256} and dv % 64 == 0 run on bf16
+ * MFMA with chunks of C; fp32 inputs with dk in {64,128,256} and dv in
+ * {64,128,256,512} run on fp32 MFMA with 16-token chunks; every other case
+ * runs on fp32 VALU arithmetic with chunks of C.  State and accumulators are
+ * fp32 throughout.
  */
 ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, const float* gamma,
                                    const float* state_in, float* state_out, void* y, int B, int H, int T,
@@ -139,8 +143,8 @@ size_t retention_chunkwise_workspace_bytes(int B, int H, int T, int dk, int dv, 
  * like there); the gradients do not depend on it beyond rounding, and the
  * kernels choose their own chunking.  State and accumulators are fp32; bf16
  * inputs with dk in {64, 128, 256} and dv in {64, 128, 256, 512} take bf16
- * MFMA products (as the forward does), fp32 inputs with those dk and dv (and
- * dk = 512) fp32 MFMA products, every other case fp32 VALU arithmetic.
+ * MFMA products (as the forward does), fp32 inputs with those dk and dv fp32
+ * MFMA products, every other case (dk <= 256, dv <= 512) fp32 VALU arithmetic.
  */
 ret_status retention_chunkwise_bwd(const void* q, const void* k, const void* v, const float* gamma,
                                    const float* state_in, const void* grad_y, const float* grad_state_out,
@@ -181,7 +185,7 @@ ret_status retention_group_norm(const void* y, const float* weight, const float*
  * ("Methodology and Architecture") calls it the O(1)-per-token inference
  * representation.
  *   q, k  : [B,H,dk] in dt.   v : [B,H,dv] in dt.
- *   state : in/out, fp32 [B,H,dk,dv]; required.
+ *   state : in/out, fp32 [B,H,dk,dv]; required; must not overlap q, k or v.
  *   y     : written, [B,H,dv] in dt; must not alias the other arguments.
  */
 ret_status retention_recurrent_step(const void* q, const void* k, const void* v, const float* gamma,

@@ -113,6 +113,16 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _out_check(t: torch.Tensor, shape, dtype, device, name):
+    """A caller-supplied output: shape and dtype first (a kernel writes exactly
+    that many elements of that size), then device and contiguity."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    _dev(t, name)
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+
+
 def _state_check(s: Optional[torch.Tensor], shape, device, name):
     if s is None:
         return
@@ -121,15 +131,26 @@ def _state_check(s: Optional[torch.Tensor], shape, device, name):
         raise ValueError(f"{name} must be float32 {tuple(shape)} on {device}")
 
 
-def _qkv(q, k, v):
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, n)
+def _qkv_shapes(q, k, v):
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("expected q, k [B,H,T,dk] and v [B,H,T,dv]")
-    if not (q.dtype == k.dtype == v.dtype) or not (q.device == k.device == v.device):
-        raise ValueError("q, k, v must share dtype and device")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
     B, H, T, dk = q.shape
     return B, H, T, dk, v.shape[-1], _dt(q)
+
+
+def _qkv_devices(q, k, v):
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must share a device")
+
+
+def _qkv(q, k, v):
+    dims = _qkv_shapes(q, k, v)
+    _qkv_devices(q, k, v)
+    return dims
 
 
 def chunkwise_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, C: int, dtype: torch.dtype) -> int:
@@ -153,7 +174,10 @@ def chunkwise_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma, C: i
     Returns (y, state_out).
     """
     lib = load()
-    B, H, T, dk, dv, dt = _qkv(q, k, v)
+    B, H, T, dk, dv, dt = _qkv_shapes(q, k, v)
+    if y is not None:
+        _out_check(y, (B, H, T, dv), q.dtype, q.device, "y")
+    _qkv_devices(q, k, v)
     sshape = (B, H, dk, dv)
     _state_check(state_in, sshape, q.device, "state_in")
     if state_out is True:
@@ -163,10 +187,6 @@ def chunkwise_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma, C: i
     _state_check(state_out, sshape, q.device, "state_out")
     if y is None:
         y = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
-    else:
-        _dev(y, "y")
-        if y.shape != (B, H, T, dv) or y.dtype != q.dtype:
-            raise ValueError("y must match [B,H,T,dv] and the input dtype")
     need = int(lib.retention_chunkwise_workspace_bytes(B, H, T, dk, dv, int(C), dt))
     ws_bytes = 0
     if need and need != ctypes.c_size_t(-1).value:
@@ -260,12 +280,13 @@ def parallel_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma,
                  state_in: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Parallel-form retention forward on the GPU (retention_parallel_fwd)."""
     lib = load()
-    B, H, T, dk, dv, dt = _qkv(q, k, v)
+    B, H, T, dk, dv, dt = _qkv_shapes(q, k, v)
+    if y is not None:
+        _out_check(y, (B, H, T, dv), q.dtype, q.device, "y")
+    _qkv_devices(q, k, v)
     _state_check(state_in, (B, H, dk, dv), q.device, "state_in")
     if y is None:
         y = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
-    else:
-        _dev(y, "y")
     st = lib.retention_parallel_fwd(_ptr(q), _ptr(k), _ptr(v), _gamma_array(gamma, H), _ptr(state_in), _ptr(y),
                                     B, H, T, dk, dv, dt, _stream(q.device))
     _check(st)
@@ -277,8 +298,6 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma, sta
     """One decode step on the GPU (retention_recurrent_step): state <- gamma*state + k^T v
     in place, returns y = q state.  q, k [B,H,dk]; v [B,H,dv]; state fp32 [B,H,dk,dv]."""
     lib = load()
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, n)
     if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
         raise ValueError("expected q, k [B,H,dk] and v [B,H,dv]")
     B, H, dk = q.shape
@@ -286,11 +305,15 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma, sta
     dt = _dt(q)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share a dtype")
+    if y is not None:
+        _out_check(y, (B, H, dv), q.dtype, q.device, "y")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must share a device")
     _state_check(state, (B, H, dk, dv), q.device, "state")
     if y is None:
         y = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
-    else:
-        _dev(y, "y")
     st = lib.retention_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _gamma_array(gamma, H), _ptr(state), _ptr(y),
                                       B, H, dk, dv, dt, _stream(q.device))
     _check(st)

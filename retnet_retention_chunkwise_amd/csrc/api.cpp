@@ -111,6 +111,10 @@ ret_status retention_recurrent_step(const void* q, const void* k, const void* v,
   if (overlap(y, ny, q, bh * dk * es) || overlap(y, ny, k, bh * dk * es) || overlap(y, ny, v, ny) ||
       overlap(y, ny, state, bh * dk * dv * 4))
     return fail(RET_ERR_INVALID_ARG, "%s: y overlaps an input or the state", fn);
+  // the state is rewritten while other workgroups still read q, k and v
+  const size_t ns = bh * dk * dv * 4;
+  if (overlap(state, ns, q, bh * dk * es) || overlap(state, ns, k, bh * dk * es) || overlap(state, ns, v, ny))
+    return fail(RET_ERR_INVALID_ARG, "%s: the state overlaps q, k or v", fn);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return for_head_groups(fn, H, gamma, [&](const ret::HeadGroup& g) {
     return ret::launch_recurrent_step(q, k, v, state, y, B, H, dk, dv, static_cast<int>(dt), g, s);

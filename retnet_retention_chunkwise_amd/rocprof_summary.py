@@ -3,6 +3,8 @@
     python -m retnet_retention_chunkwise_amd.rocprof_summary stats <kernel_stats.csv> [--cmd "..."]
     python -m retnet_retention_chunkwise_amd.rocprof_summary traffic --fetch <dir> --write <dir> \
         --kernel '<name substring>[|<substring>...]' --source <kernel .hip> --copy-mib <N> [--cmd "..."]
+    python -m retnet_retention_chunkwise_amd.rocprof_summary mfma --pmc <dir> --stats <kernel_stats.csv> \
+        --kernel '<name substring>' [--cmd "..."]
 
 `stats` turns a `--kernel-trace --stats` kernel_stats.csv into a short text
 table.  `traffic` turns two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs into
@@ -12,6 +14,12 @@ argument lists hold commas), calibrated against a plain copy of
 `--copy-mib` MiB measured in the same runs (bytes = counter * known copy bytes /
 copy's counter), and records the sha256 of the kernel source so that a reader
 can tell whether the figures still describe the current kernel.
+`mfma` turns a `--pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES
+GRBM_GUI_ACTIVE` run into the bf16 MFMA work a kernel executes per launch
+(MOPS counts units of 512 flops) and, with its average duration from a kernel
+trace, the executed MFMA rate against the 2.5 PFLOP/s dense bf16 peak, plus the
+MFMA-busy share of SIMD cycles (busy cycles over active cycles x 256 CUs x 4
+SIMDs).
 """
 from __future__ import annotations
 
@@ -106,6 +114,55 @@ def traffic(fetch_dir, write_dir, kernel, source, copy_mib, copy_substr="copy", 
     return "\n".join(lines) + "\n"
 
 
+def _per_dispatch_all(directory: str):
+    """{(file, dispatch): {counter: value}} and their kernel names."""
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {directory}")
+    acc = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            key = (f, r["Dispatch_Id"])
+            acc[key][r["Counter_Name"]] += float(r["Counter_Value"])
+            names[key] = r["Kernel_Name"]
+    return acc, names
+
+
+def mfma(pmc_dir, stats_csv, kernel, cmd="", peak_tflops=2500.0, cus=256, simds=4):
+    acc, names = _per_dispatch_all(pmc_dir)
+    keys = [k for k in acc if kernel in names[k]]
+    if not keys:
+        raise ValueError(f"no dispatch of a kernel matching '{kernel}'")
+    mean = lambda c: sum(acc[k].get(c, 0.0) for k in keys) / len(keys)
+    mops = mean("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    busy = mean("SQ_VALU_MFMA_BUSY_CYCLES")
+    active = mean("GRBM_GUI_ACTIVE")
+    rows = [r for r in csv.DictReader(open(stats_csv)) if kernel in r["Name"]]
+    if not rows:
+        raise ValueError(f"no kernel matching '{kernel}' in {stats_csv}")
+    calls = sum(int(r["Calls"]) for r in rows)
+    avg_ns = sum(float(r["AverageNs"]) * int(r["Calls"]) for r in rows) / calls
+    flops = mops * 512.0
+    tflops = flops / (avg_ns * 1e-9) / 1e12
+    lines = []
+    if cmd:
+        lines.append(f"command: {cmd}")
+    lines += [
+        f"kernel: {kernel}",
+        f"dispatches_averaged: {len(keys)} (counters), {calls} (trace)",
+        f"SQ_INSTS_VALU_MFMA_MOPS_BF16_per_launch: {mops:.0f}",
+        f"SQ_VALU_MFMA_BUSY_CYCLES_per_launch: {busy:.0f}",
+        f"GRBM_GUI_ACTIVE_per_launch: {active:.0f}",
+        f"kernel_avg_us (trace): {avg_ns / 1e3:.2f}",
+        f"executed_bf16_mfma_flops_per_launch: {flops:.4e}",
+        f"executed_bf16_mfma_tflops: {tflops:.1f}",
+        f"executed_mfma_frac_of_{peak_tflops:.0f}_tflops: {tflops / peak_tflops:.4f}",
+        f"mfma_busy_frac (busy / (active x {cus} CUs x {simds} SIMDs)): {busy / (active * cus * simds):.4f}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
 def read_traffic_file(path: str):
     """Parse a `traffic` summary back into a dict (used by bench.py)."""
     out = {}
@@ -130,9 +187,16 @@ def main(argv=None):
     t.add_argument("--copy-mib", type=float, required=True)
     t.add_argument("--copy-kernel", default="copy")
     t.add_argument("--cmd", default="")
+    m = sub.add_parser("mfma")
+    m.add_argument("--pmc", required=True)
+    m.add_argument("--stats", required=True)
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--cmd", default="")
     a = ap.parse_args(argv)
     if a.cmd_name == "stats":
         sys.stdout.write(stats_table(a.csv, a.cmd))
+    elif a.cmd_name == "mfma":
+        sys.stdout.write(mfma(a.pmc, a.stats, a.kernel, a.cmd))
     else:
         sys.stdout.write(traffic(a.fetch, a.write, a.kernel, a.source, a.copy_mib, a.copy_kernel, a.cmd))
 

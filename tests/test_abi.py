@@ -299,3 +299,37 @@ def test_segmented_backward_requires_workspace(lib):
     st = lib.retention_chunkwise_bwd(q, k, v, gam(0.5, 0.9), None, dy, None, gq, gk, gv, None, 1, 2, 4096, 64, 64, 64,
                                      1, ctypes.c_void_p((1 << 36) + 4096), need, None)
     assert st == INVALID and "workspace overlaps" in _lib.last_error()
+
+
+@pytest.mark.parametrize("bad", ["shape", "dtype"])
+def test_python_wrapper_checks_caller_outputs_before_any_launch(bad):
+    """A caller-supplied y of the wrong shape or dtype is refused with
+    ValueError before any device work: the kernels write exactly B*H*(T)*dv
+    elements of the input dtype into it."""
+    import torch
+
+    B, H, T, dk, dv = 1, 2, 5, 4, 6
+    q = torch.zeros(B, H, T, dk)
+    v = torch.zeros(B, H, T, dv)
+    st = torch.zeros(B, H, dk, dv)
+    wrong_y = (torch.zeros(B, H, T, dv - 1) if bad == "shape" else torch.zeros(B, H, T, dv, dtype=torch.bfloat16))
+    for call in (lambda: _lib.parallel_fwd(q, q, v, [0.5, 0.5], y=wrong_y),
+                 lambda: _lib.chunkwise_fwd(q, q, v, [0.5, 0.5], 4, y=wrong_y)):
+        with pytest.raises(ValueError, match="y must be"):
+            call()
+    wrong_step_y = (torch.zeros(B, H, dv + 1) if bad == "shape" else torch.zeros(B, H, dv, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="y must be"):
+        _lib.recurrent_step(q[:, :, 0], q[:, :, 0], v[:, :, 0], [0.5, 0.5], st, y=wrong_step_y)
+
+
+def test_recurrent_step_rejects_state_overlapping_inputs(lib):
+    """The decode step rewrites the state in place while other workgroups read
+    q, k and v: a state overlapping any of them is refused."""
+    B, H, dk, dv = 1, 1, 4, 4
+    base = 0x100000
+    q, k, v = (ctypes.c_void_p(base + i * 0x1000) for i in range(3))
+    y = ctypes.c_void_p(0x900000)
+    for overlapped in (0, 1, 2):
+        st_ptr = ctypes.c_void_p(base + overlapped * 0x1000)
+        st = lib.retention_recurrent_step(q, k, v, gam(0.5), st_ptr, y, B, H, dk, dv, 0, None)
+        assert st == INVALID and "the state overlaps" in _lib.last_error(), _lib.last_error()
