@@ -117,6 +117,28 @@ ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, 
 size_t retention_chunkwise_workspace_bytes(int B, int H, int T, int dk, int dv, int C, ret_dtype dt);
 
 /*
+ * retention_chunkwise_fwd without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Arguments, results, validation and
+ * kernels are those of retention_chunkwise_fwd.  A call that needs a workspace
+ * (retention_chunkwise_workspace_bytes() > 0: the segmented calls) uses a
+ * static device array of RET_NOALLOC_SCRATCH_BYTES bytes inside the library
+ * instead; each GPU the library runs on holds its own copy until the process
+ * ends.  A call whose workspace would exceed it returns RET_ERR_UNSUPPORTED
+ * (the long-context workload B1 H8 T65536 dk256 dv512 C128 needs exactly
+ * 64 MiB and fits).  Nothing is allocated: no hipMalloc, hipFree or allocating
+ * library routine is called.  All calls on one GPU share that GPU's array:
+ * calls ordered on one stream are safe, but calls that overlap in time on one
+ * GPU (several streams, or several host threads) race on it and give
+ * undefined results.  Its contents on entry are ignored (every slot a call
+ * reads was written earlier in the same call).
+ */
+#define RET_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ret_status retention_chunkwise_fwd_noalloc(const void* q, const void* k, const void* v, const float* gamma,
+                                           const float* state_in, float* state_out, void* y, int B, int H,
+                                           int T, int dk, int dv, int C, ret_dtype dt, void* stream);
+
+/*
  * Backward of the chunkwise form: the gradients of retention_chunkwise_fwd for
  * the loss L = sum <grad_y, y> + <grad_state_out, state_out>.  The aimpact page
  * ("Il meccanismo") says the parallel form is the one run in parallel for

@@ -4,6 +4,8 @@ The compute lives in hand-written HIP kernels behind a C ABI
 (include/libretention.h); this package is the thin Python binding:
 
     chunkwise_fwd(q, k, v, gamma, C, state_in=None, state_out=True) -> (y, state_out)
+    chunkwise_fwd_noalloc(q, k, v, gamma, C, state_in=None, state_out=None, y=None) -> y
+        (the same with no allocation inside the call: static device scratch)
     chunkwise_bwd(q, k, v, gamma, C, grad_y, state_in=None, grad_state_out=None)
         -> (grad_q, grad_k, grad_v, grad_state_in)
     parallel_fwd(q, k, v, gamma, state_in=None) -> y
@@ -20,6 +22,7 @@ from ._lib import (  # noqa: F401
     RetentionError,
     chunkwise_bwd,
     chunkwise_fwd,
+    chunkwise_fwd_noalloc,
     chunkwise_workspace_bytes,
     group_norm,
     last_error,

@@ -27,6 +27,7 @@ SIGNATURES = {
     "retention_parallel_fwd": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "retention_chunkwise_fwd": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "retention_chunkwise_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "retention_chunkwise_fwd_noalloc": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "retention_recurrent_step": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "retention_group_norm": (_i, [_vp, _vp, _vp, ctypes.c_float, _vp, _i, _i, _i, _i, _i, _vp]),
     "retention_chunkwise_bwd": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
@@ -200,6 +201,29 @@ def chunkwise_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma, C: i
                                      ws_bytes, _stream(q.device))
     _check(st)
     return y, state_out
+
+
+def chunkwise_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma, C: int,
+                          state_in: Optional[torch.Tensor] = None, state_out: Optional[torch.Tensor] = None,
+                          y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """retention_chunkwise_fwd_noalloc: chunkwise_fwd with the workspace of
+    segmented calls in the library's static device scratch, so that the call
+    itself allocates nothing (pass y and, if wanted, state_out preallocated).
+    Calls that overlap in time on one GPU race on that scratch.  Returns y."""
+    lib = load()
+    B, H, T, dk, dv, dt = _qkv_shapes(q, k, v)
+    if y is not None:
+        _out_check(y, (B, H, T, dv), q.dtype, q.device, "y")
+    _qkv_devices(q, k, v)
+    sshape = (B, H, dk, dv)
+    _state_check(state_in, sshape, q.device, "state_in")
+    _state_check(state_out, sshape, q.device, "state_out")
+    if y is None:
+        y = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    _check(lib.retention_chunkwise_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _gamma_array(gamma, H), _ptr(state_in),
+                                               _ptr(state_out), _ptr(y), B, H, T, dk, dv, int(C), dt,
+                                               _stream(q.device)))
+    return y
 
 
 def chunkwise_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma, C: int, grad_y: torch.Tensor,

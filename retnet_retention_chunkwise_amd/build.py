@@ -34,6 +34,7 @@ SOURCES = [
     "group_norm.hip",
     "chunkwise_f32_mfma.hip",
     "short_mfma.hip",
+    "noalloc.hip",
 ]
 
 ARCH = "gfx950"

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <string>
 
+#include "abi_internal.h"
 #include "kernels.h"
 #include "libretention.h"
 
@@ -91,6 +92,98 @@ HeadDecay make_head_decay(const HeadGroup& g) {
 }
 }  // namespace ret
 
+namespace ret {
+
+void set_last_error(const char* text) { g_last_error = text; }
+
+// Validation of a chunkwise forward call: sizes, pointers, aliasing and (when
+// check_ws) the caller's workspace.  Makes no HIP call.
+ret_status chunkwise_fwd_check(const ChunkwiseFwdArgs& a, const void* workspace, size_t workspace_bytes,
+                               bool check_ws) {
+  const char* fn = check_ws ? "retention_chunkwise_fwd" : "retention_chunkwise_fwd_noalloc";
+  const int B = a.B, H = a.H, T = a.T, dk = a.dk, dv = a.dv, C = a.C;
+  const ret_dtype dt = static_cast<ret_dtype>(a.dt);
+  ret_status st = check_common(fn, B, H, T, dk, dv, dt, a.gamma);
+  if (st != RET_OK) return st;
+  if (C < 1) return fail(RET_ERR_INVALID_ARG, "%s: chunk length C=%d must be >= 1", fn, C);
+  if (C > RET_MAX_CHUNK) return fail(RET_ERR_UNSUPPORTED, "%s: chunk length C=%d exceeds %d", fn, C, RET_MAX_CHUNK);
+  if (T > 0 && (!a.q || !a.k || !a.v || !a.y)) return fail(RET_ERR_INVALID_ARG, "%s: q, k, v and y are required", fn);
+  if (misaligned(a.q) || misaligned(a.k) || misaligned(a.v) || misaligned(a.y) || misaligned(a.state_in) ||
+      misaligned(a.state_out) || (check_ws && misaligned(workspace)))
+    return fail(RET_ERR_UNSUPPORTED, "%s: tensor pointers must be 16-byte aligned", fn);
+  const size_t es = dsize(dt);
+  const size_t bht = static_cast<size_t>(B) * H * T;
+  const size_t ny = bht * dv * es;
+  const size_t ns = static_cast<size_t>(B) * H * dk * dv * 4;
+  if (overlap(a.y, ny, a.q, bht * dk * es) || overlap(a.y, ny, a.k, bht * dk * es) || overlap(a.y, ny, a.v, ny) ||
+      overlap(a.y, ny, a.state_in, ns) || overlap(a.y, ny, a.state_out, ns))
+    return fail(RET_ERR_INVALID_ARG, "%s: y overlaps an input or a state buffer", fn);
+  if (a.state_in != a.state_out && overlap(a.state_in, ns, a.state_out, ns))
+    return fail(RET_ERR_INVALID_ARG, "%s: state_in and state_out overlap without being the same buffer", fn);
+  if (a.state_out != nullptr && (overlap(a.state_out, ns, a.q, bht * dk * es) ||
+                                 overlap(a.state_out, ns, a.k, bht * dk * es) || overlap(a.state_out, ns, a.v, ny)))
+    return fail(RET_ERR_INVALID_ARG, "%s: state_out overlaps an input", fn);
+  if (!check_ws) return RET_OK;
+  const size_t need = retention_chunkwise_workspace_bytes(B, H, T, dk, dv, C, dt);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(RET_ERR_INVALID_ARG, "%s: workspace of %zu bytes required, %zu given", fn, need, workspace_bytes);
+  if (need > 0 && (overlap(workspace, need, a.y, ny) || overlap(workspace, need, a.q, bht * dk * es) ||
+                   overlap(workspace, need, a.k, bht * dk * es) || overlap(workspace, need, a.v, ny) ||
+                   overlap(workspace, need, a.state_in, ns) || overlap(workspace, need, a.state_out, ns)))
+    return fail(RET_ERR_INVALID_ARG, "%s: workspace overlaps another argument", fn);
+  return RET_OK;
+}
+
+// Kernel choice and launch of a validated chunkwise forward call; workspace
+// holds retention_chunkwise_workspace_bytes() bytes when that is non-zero.
+ret_status chunkwise_fwd_run(const ChunkwiseFwdArgs& a, void* workspace, void* stream) {
+  const char* fn = "retention_chunkwise_fwd";
+  const void *q = a.q, *k = a.k, *v = a.v;
+  const float* state_in = a.state_in;
+  float* state_out = a.state_out;
+  void* y = a.y;
+  const int B = a.B, H = a.H, T = a.T, dk = a.dk, dv = a.dv, C = a.C, dt = a.dt;
+  const size_t ns = static_cast<size_t>(B) * H * dk * dv * 4;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    if (state_out == nullptr || state_out == state_in) return ok();
+    const hipError_t e = launch_state_copy(state_in, state_out, ns / 4, s);
+    return e == hipSuccess ? ok() : hip_fail(fn, e);
+  }
+  if (T == 1 && state_in != nullptr && state_in == state_out) {
+    // one token continued in place: exactly the recurrent step
+    return for_head_groups(fn, H, a.gamma, [&](const HeadGroup& g) {
+      return launch_recurrent_step(q, k, v, state_out, y, B, H, dk, dv, dt, g, s);
+    });
+  }
+  if (T >= kShortMfmaMinT && short_mfma_supports(T, dk, dv)) {
+    // one chunk of T tokens on fp32 MFMA (the same result as any C up to rounding order)
+    return for_head_groups(fn, H, a.gamma, [&](const HeadGroup& g) {
+      return launch_short_mfma(q, k, v, state_in, state_out, y, B, H, T, dk, dv, dt, g, s);
+    });
+  }
+  if (T <= kShortChunkMaxT) {
+    // one chunk of T tokens (the same result as any C up to rounding order)
+    return for_head_groups(fn, H, a.gamma, [&](const HeadGroup& g) {
+      return launch_short_chunk(q, k, v, state_in, state_out, y, B, H, T, dk, dv, dt, g, s);
+    });
+  }
+  const bool mfma = chunkwise_mfma_supports(T, dk, dv, C, dt);
+  const bool f32 = chunkwise_f32_mfma_supports(dk, dv, dt);
+  const ChunkSegments segs = mfma ? chunkwise_mfma_segments(B, H, T, dv, C) : ChunkSegments{T, 1, 1};
+  float* ws = static_cast<float*>(workspace);
+  return for_head_groups(fn, H, a.gamma, [&](const HeadGroup& g) {
+    if (mfma) return launch_chunkwise_mfma(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, segs, ws, g, s);
+    if (f32)
+      return launch_chunkwise_f32_fwd(static_cast<const float*>(q), static_cast<const float*>(k),
+                                      static_cast<const float*>(v), state_in, state_out, static_cast<float*>(y), B,
+                                      H, T, dk, dv, g, s);
+    return launch_chunkwise_generic(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, dt, g, s);
+  });
+}
+
+}  // namespace ret
+
 extern "C" {
 
 const char* retention_last_error(void) { return g_last_error.c_str(); }
@@ -157,71 +250,10 @@ ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, 
                                    const float* state_in, float* state_out, void* y, int B, int H, int T, int dk,
                                    int dv, int C, ret_dtype dt, void* workspace, size_t workspace_bytes,
                                    void* stream) {
-  const char* fn = "retention_chunkwise_fwd";
-  ret_status st = check_common(fn, B, H, T, dk, dv, dt, gamma);
+  const ret::ChunkwiseFwdArgs a{q, k, v, gamma, state_in, state_out, y, B, H, T, dk, dv, C, static_cast<int>(dt)};
+  const ret_status st = ret::chunkwise_fwd_check(a, workspace, workspace_bytes, true);
   if (st != RET_OK) return st;
-  if (C < 1) return fail(RET_ERR_INVALID_ARG, "%s: chunk length C=%d must be >= 1", fn, C);
-  if (C > RET_MAX_CHUNK) return fail(RET_ERR_UNSUPPORTED, "%s: chunk length C=%d exceeds %d", fn, C, RET_MAX_CHUNK);
-  if (T > 0 && (!q || !k || !v || !y)) return fail(RET_ERR_INVALID_ARG, "%s: q, k, v and y are required", fn);
-  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(y) || misaligned(state_in) ||
-      misaligned(state_out) || misaligned(workspace))
-    return fail(RET_ERR_UNSUPPORTED, "%s: tensor pointers must be 16-byte aligned", fn);
-  const size_t need = retention_chunkwise_workspace_bytes(B, H, T, dk, dv, C, dt);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(RET_ERR_INVALID_ARG, "%s: workspace of %zu bytes required, %zu given", fn, need, workspace_bytes);
-  const size_t es = dsize(dt);
-  const size_t bht = static_cast<size_t>(B) * H * T;
-  const size_t ny = bht * dv * es;
-  const size_t ns = static_cast<size_t>(B) * H * dk * dv * 4;
-  if (overlap(y, ny, q, bht * dk * es) || overlap(y, ny, k, bht * dk * es) || overlap(y, ny, v, ny) ||
-      overlap(y, ny, state_in, ns) || overlap(y, ny, state_out, ns))
-    return fail(RET_ERR_INVALID_ARG, "%s: y overlaps an input or a state buffer", fn);
-  if (need > 0 && (overlap(workspace, need, y, ny) || overlap(workspace, need, q, bht * dk * es) ||
-                   overlap(workspace, need, k, bht * dk * es) || overlap(workspace, need, v, ny) ||
-                   overlap(workspace, need, state_in, ns) || overlap(workspace, need, state_out, ns)))
-    return fail(RET_ERR_INVALID_ARG, "%s: workspace overlaps another argument", fn);
-  if (state_in != state_out && overlap(state_in, ns, state_out, ns))
-    return fail(RET_ERR_INVALID_ARG, "%s: state_in and state_out overlap without being the same buffer", fn);
-  if (state_out != nullptr && (overlap(state_out, ns, q, bht * dk * es) || overlap(state_out, ns, k, bht * dk * es) ||
-                               overlap(state_out, ns, v, ny)))
-    return fail(RET_ERR_INVALID_ARG, "%s: state_out overlaps an input", fn);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (T == 0) {
-    if (state_out == nullptr || state_out == state_in) return ok();
-    const hipError_t e = ret::launch_state_copy(state_in, state_out, ns / 4, s);
-    return e == hipSuccess ? ok() : hip_fail(fn, e);
-  }
-  if (T == 1 && state_in != nullptr && state_in == state_out) {
-    // one token continued in place: exactly the recurrent step
-    return for_head_groups(fn, H, gamma, [&](const ret::HeadGroup& g) {
-      return ret::launch_recurrent_step(q, k, v, state_out, y, B, H, dk, dv, static_cast<int>(dt), g, s);
-    });
-  }
-  if (T >= ret::kShortMfmaMinT && ret::short_mfma_supports(T, dk, dv)) {
-    // one chunk of T tokens on fp32 MFMA (the same result as any C up to rounding order)
-    return for_head_groups(fn, H, gamma, [&](const ret::HeadGroup& g) {
-      return ret::launch_short_mfma(q, k, v, state_in, state_out, y, B, H, T, dk, dv, static_cast<int>(dt), g, s);
-    });
-  }
-  if (T <= ret::kShortChunkMaxT) {
-    // one chunk of T tokens (the same result as any C up to rounding order)
-    return for_head_groups(fn, H, gamma, [&](const ret::HeadGroup& g) {
-      return ret::launch_short_chunk(q, k, v, state_in, state_out, y, B, H, T, dk, dv, static_cast<int>(dt), g, s);
-    });
-  }
-  const bool mfma = ret::chunkwise_mfma_supports(T, dk, dv, C, static_cast<int>(dt));
-  const bool f32 = ret::chunkwise_f32_mfma_supports(dk, dv, static_cast<int>(dt));
-  const ret::ChunkSegments segs = mfma ? ret::chunkwise_mfma_segments(B, H, T, dv, C) : ret::ChunkSegments{T, 1, 1};
-  float* ws = static_cast<float*>(workspace);
-  return for_head_groups(fn, H, gamma, [&](const ret::HeadGroup& g) {
-    if (mfma) return ret::launch_chunkwise_mfma(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, segs, ws, g, s);
-    if (f32)
-      return ret::launch_chunkwise_f32_fwd(static_cast<const float*>(q), static_cast<const float*>(k),
-                                           static_cast<const float*>(v), state_in, state_out, static_cast<float*>(y),
-                                           B, H, T, dk, dv, g, s);
-    return ret::launch_chunkwise_generic(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, static_cast<int>(dt),
-                                         g, s);
-  });
+  return ret::chunkwise_fwd_run(a, workspace, stream);
 }
 
 size_t retention_chunkwise_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C, ret_dtype dt) {

@@ -333,3 +333,23 @@ def test_recurrent_step_rejects_state_overlapping_inputs(lib):
         st_ptr = ctypes.c_void_p(base + overlapped * 0x1000)
         st = lib.retention_recurrent_step(q, k, v, gam(0.5), st_ptr, y, B, H, dk, dv, 0, None)
         assert st == INVALID and "the state overlaps" in _lib.last_error(), _lib.last_error()
+
+
+def test_noalloc_rejects_calls_beyond_its_static_scratch(lib):
+    """retention_chunkwise_fwd_noalloc refuses, before any HIP call, a call whose
+    workspace would exceed the static scratch, and names both sizes; the
+    long-context workload (B1 H8 T65536 dk256 dv512 C128) fits exactly."""
+    limit = 64 << 20
+    assert lib.retention_chunkwise_workspace_bytes(1, 8, 65536, 256, 512, 128, 1) == limit
+    # 31 heads x 8 column tiles = 248 walkers: 2 segments, 4 sub-segments -> 6 slots of 15.5 MiB
+    need = lib.retention_chunkwise_workspace_bytes(1, 31, 65536, 256, 512, 128, 1)
+    assert need > limit
+    q, k, v, y = (ctypes.c_void_p(a << 36) for a in (1, 2, 3, 4))
+    st = lib.retention_chunkwise_fwd_noalloc(q, k, v, gam(*([0.9] * 31)), None, None, y, 1, 31, 65536, 256, 512,
+                                             128, 1, None)
+    assert st == UNSUPPORTED
+    msg = _lib.last_error()
+    assert "static scratch" in msg and str(need) in msg and str(limit) in msg, msg
+    # argument errors are reported as by retention_chunkwise_fwd
+    st = lib.retention_chunkwise_fwd_noalloc(None, k, v, gam(0.5), None, None, y, 1, 1, 8, 16, 16, 4, 0, None)
+    assert st == INVALID and "required" in _lib.last_error()
