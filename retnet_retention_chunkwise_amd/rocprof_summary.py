@@ -18,8 +18,9 @@ can tell whether the figures still describe the current kernel.
 GRBM_GUI_ACTIVE` run into the bf16 MFMA work a kernel executes per launch
 (MOPS counts units of 512 flops) and, with its average duration from a kernel
 trace, the executed MFMA rate against the 2.5 PFLOP/s dense bf16 peak, plus the
-MFMA-busy share of SIMD cycles (busy cycles over active cycles x 256 CUs x 4
-SIMDs).
+MFMA-busy share of SIMD cycles (busy cycles over the per-XCD active cycles x
+1024 SIMDs; GRBM_GUI_ACTIVE sums the 8 XCDs, which the implied clock, active
+cycles / 8 / duration, shows).
 """
 from __future__ import annotations
 
@@ -129,15 +130,29 @@ def _per_dispatch_all(directory: str):
     return acc, names
 
 
-def mfma(pmc_dir, stats_csv, kernel, cmd="", peak_tflops=2500.0, cus=256, simds=4):
-    acc, names = _per_dispatch_all(pmc_dir)
-    keys = [k for k in acc if kernel in names[k]]
-    if not keys:
+def mfma(pmc_dir, stats_csv, kernel, cmd="", peak_tflops=2500.0, xcds=8, simds=1024):
+    """MFMA work and busy share of one kernel from a counter run (and its
+    steady-state duration from a kernel-trace stats file)."""
+    files = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {pmc_dir}")
+    acc = collections.defaultdict(lambda: collections.defaultdict(float))
+    dur = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            key = (f, r["Dispatch_Id"])
+            acc[key][r["Counter_Name"]] += float(r["Counter_Value"])
+            dur[key] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    if not acc:
         raise ValueError(f"no dispatch of a kernel matching '{kernel}'")
+    keys = list(acc)
     mean = lambda c: sum(acc[k].get(c, 0.0) for k in keys) / len(keys)
     mops = mean("SQ_INSTS_VALU_MFMA_MOPS_BF16")
     busy = mean("SQ_VALU_MFMA_BUSY_CYCLES")
     active = mean("GRBM_GUI_ACTIVE")
+    pmc_ns = sum(dur[k] for k in keys) / len(keys)
     rows = [r for r in csv.DictReader(open(stats_csv)) if kernel in r["Name"]]
     if not rows:
         raise ValueError(f"no kernel matching '{kernel}' in {stats_csv}")
@@ -145,6 +160,7 @@ def mfma(pmc_dir, stats_csv, kernel, cmd="", peak_tflops=2500.0, cus=256, simds=
     avg_ns = sum(float(r["AverageNs"]) * int(r["Calls"]) for r in rows) / calls
     flops = mops * 512.0
     tflops = flops / (avg_ns * 1e-9) / 1e12
+    per_xcd = active / xcds
     lines = []
     if cmd:
         lines.append(f"command: {cmd}")
@@ -153,12 +169,13 @@ def mfma(pmc_dir, stats_csv, kernel, cmd="", peak_tflops=2500.0, cus=256, simds=
         f"dispatches_averaged: {len(keys)} (counters), {calls} (trace)",
         f"SQ_INSTS_VALU_MFMA_MOPS_BF16_per_launch: {mops:.0f}",
         f"SQ_VALU_MFMA_BUSY_CYCLES_per_launch: {busy:.0f}",
-        f"GRBM_GUI_ACTIVE_per_launch: {active:.0f}",
+        f"GRBM_GUI_ACTIVE_per_launch: {active:.0f} (summed over {xcds} XCDs)",
+        f"counter_run_kernel_us: {pmc_ns / 1e3:.2f} (clock {per_xcd / pmc_ns:.2f} GHz = GRBM_GUI_ACTIVE / {xcds} / duration)",
         f"kernel_avg_us (trace): {avg_ns / 1e3:.2f}",
-        f"executed_bf16_mfma_flops_per_launch: {flops:.4e}",
-        f"executed_bf16_mfma_tflops: {tflops:.1f}",
+        f"executed_bf16_mfma_flops_per_launch: {flops:.4e} (MOPS x 512)",
+        f"executed_bf16_mfma_tflops: {tflops:.1f} (executed flops / trace average duration)",
         f"executed_mfma_frac_of_{peak_tflops:.0f}_tflops: {tflops / peak_tflops:.4f}",
-        f"mfma_busy_frac (busy / (active x {cus} CUs x {simds} SIMDs)): {busy / (active * cus * simds):.4f}",
+        f"mfma_busy_frac: {busy / (per_xcd * simds):.4f} (busy cycles / (GRBM_GUI_ACTIVE / {xcds} x {simds} SIMDs))",
     ]
     return "\n".join(lines) + "\n"
 
