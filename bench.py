@@ -17,7 +17,7 @@ Measured in the same run, each in an object of its own with its roofline:
   layer6p7b    chunkwise B2 H16 T8192 C=128 (805 MB, one input set)
   layer1p3b    chunkwise B4 H8 T2048 C=64 (201 MB, four rotating input sets)
   decode       1000 chained recurrent steps, batch 128, H16, fp32 state
-  continuation 16 new tokens per decode stream from the carried state
+  continuation 16 (and 32, 64) new tokens per decode stream from the carried state
   backward     dQ, dK, dV, dS_in of the layer1p3b workload
   group_norm   per-head GroupNorm of a layer1p3b output
 
@@ -271,8 +271,10 @@ def bench_decode(dev, decode_steps):
     }
 
 
-def bench_continuation(dev, ct=16):
-    """chunkwise on ct new tokens per stream from the decode state, in place"""
+def bench_continuation(dev, tokens=(16, 32, 64)):
+    """chunkwise on T new tokens per stream from the decode state, in place,
+    for each T in tokens (the bf16 MFMA streaming kernel); the first T is the
+    object's own figure, every T is listed in "by_tokens"."""
     import torch
 
     import retnet_retention_chunkwise_amd as ret
@@ -280,30 +282,37 @@ def bench_continuation(dev, ct=16):
 
     dw = WORKLOADS["decode"]
     *_, s0 = make_decode_inputs(dw.B, dw.H, dw.dk, dw.dv, 1, dw.dtype, seed=0)
-    cq, ck, cv = (t.to(dev) for t in make_inputs(dw.B, dw.H, ct, dw.dk, dw.dv, dw.dtype, seed=1))
     cstate = s0.to(dev)
-    cy = torch.empty(dw.B, dw.H, ct, dw.dv, dtype=cq.dtype, device=dev)
     gd = list(dw.gammas)
     stream = torch.cuda.current_stream(dev)
-    call = lambda i: ret.chunkwise_fwd(cq, ck, cv, gd, ct, state_in=cstate, state_out=cstate, y=cy)
-    for i in range(3):
-        call(i)
-    torch.cuda.synchronize()
-    _, ms_pairs = eager_time_ms(call, 20, stream)
-    us = ms_pairs * 1e3
     state_bytes = dw.B * dw.H * dw.dk * dw.dv * 4
-    nbytes = 2 * state_bytes + dw.B * dw.H * ct * (2 * dw.dk + 2 * dw.dk + 2 * dw.dv + 2 * dw.dv)
-    gbs = nbytes / (us * 1e-6) / 1e9
-    traffic = load_traffic(f"short_mfma_continuation{ct}_traffic.txt", os.path.join(CSRC, "short_mfma.hip"))
-    del cq, ck, cv, cstate, cy
+    rows = []
+    for ct in tokens:
+        cq, ck, cv = (t.to(dev) for t in make_inputs(dw.B, dw.H, ct, dw.dk, dw.dv, dw.dtype, seed=1))
+        cy = torch.empty(dw.B, dw.H, ct, dw.dv, dtype=cq.dtype, device=dev)
+        call = lambda i: ret.chunkwise_fwd(cq, ck, cv, gd, ct, state_in=cstate, state_out=cstate, y=cy)
+        for i in range(3):
+            call(i)
+        torch.cuda.synchronize()
+        _, ms_pairs = eager_time_ms(call, 20, stream)
+        us = ms_pairs * 1e3
+        nbytes = 2 * state_bytes + dw.B * dw.H * ct * (2 * dw.dk + 2 * dw.dk + 2 * dw.dv + 2 * dw.dv)
+        rows.append({"tokens": ct, "kernel_us": us, "tokens_per_s": dw.B * ct / (us * 1e-6),
+                     "achieved_gbs": nbytes / (us * 1e-6) / 1e9, "algorithmic_bytes_per_launch": nbytes})
+        del cq, ck, cv, cy
+    del cstate
     torch.cuda.empty_cache()
+    h = rows[0]
+    traffic = load_traffic(f"short_bf16_continuation{h['tokens']}_traffic.txt", os.path.join(CSRC, "short_bf16.hip"))
     return {
-        "workload": f"chunkwise fwd on {ct} new tokens per stream from a carried state, in place: batch 128, H=16, "
-                    "fp32 state 256x512 per head, bf16 q/k/v",
-        "tokens_per_s": dw.B * ct / (us * 1e-6),
-        "kernel_us": us,
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic, "algorithmic_bytes_per_launch": nbytes},
+        "workload": f"chunkwise fwd on {h['tokens']} new tokens per stream from a carried state, in place: batch 128, "
+                    "H=16, fp32 state 256x512 per head, bf16 q/k/v (also 32 and 64 tokens in by_tokens)",
+        "tokens_per_s": h["tokens_per_s"],
+        "kernel_us": h["kernel_us"],
+        "roofline": {"bound": "hbm", "achieved": h["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": h["achieved_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": h["algorithmic_bytes_per_launch"]},
+        "by_tokens": rows,
     }
 
 

@@ -35,6 +35,7 @@ SOURCES = [
     "chunkwise_f32_mfma.hip",
     "short_mfma.hip",
     "noalloc.hip",
+    "short_bf16.hip",
 ]
 
 ARCH = "gfx950"

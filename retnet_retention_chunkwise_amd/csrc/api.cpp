@@ -156,6 +156,12 @@ ret_status chunkwise_fwd_run(const ChunkwiseFwdArgs& a, void* workspace, void* s
       return launch_recurrent_step(q, k, v, state_out, y, B, H, dk, dv, dt, g, s);
     });
   }
+  if (short_bf16_supports(T, dk, dv, dt)) {
+    // one chunk of T tokens on bf16 MFMA (the same result as any C up to rounding)
+    return for_head_groups(fn, H, a.gamma, [&](const HeadGroup& g) {
+      return launch_short_bf16(q, k, v, state_in, state_out, y, B, H, T, dk, dv, g, s);
+    });
+  }
   if (T >= kShortMfmaMinT && short_mfma_supports(T, dk, dv)) {
     // one chunk of T tokens on fp32 MFMA (the same result as any C up to rounding order)
     return for_head_groups(fn, H, a.gamma, [&](const HeadGroup& g) {
@@ -241,6 +247,7 @@ size_t retention_chunkwise_workspace_bytes(int B, int H, int T, int dk, int dv, 
   if (dk > RET_MAX_DK || dv > RET_MAX_DV || C > RET_MAX_CHUNK) return static_cast<size_t>(-1);
   if (dt != RET_F32 && dt != RET_BF16) return static_cast<size_t>(-1);
   if (T <= ret::kShortChunkMaxT || !ret::chunkwise_mfma_supports(T, dk, dv, C, static_cast<int>(dt))) return 0;
+  if (ret::short_bf16_supports(T, dk, dv, static_cast<int>(dt))) return 0;
   if (T <= ret::kShortMfmaMaxT && T >= ret::kShortMfmaMinT && ret::short_mfma_supports(T, dk, dv)) return 0;
   const ret::ChunkSegments segs = ret::chunkwise_mfma_segments(B, H, T, dv, C);
   return ret::chunkwise_segment_slots(segs) * B * H * dk * dv * sizeof(float);

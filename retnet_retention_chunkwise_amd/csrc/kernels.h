@@ -140,6 +140,13 @@ bool short_mfma_supports(int T, int dk, int dv);
 hipError_t launch_short_mfma(const void* q, const void* k, const void* v, const float* state_in, float* state_out,
                              void* y, int B, int H, int T, int dk, int dv, int dt, const HeadGroup& g, hipStream_t s);
 
+// bf16 inputs, 1 <= T <= kShortBf16MaxT, dk % 32 == 0, dv % 64 == 0: the same
+// one-chunk streaming pass with bf16 MFMA products.
+constexpr int kShortBf16MaxT = 64;
+bool short_bf16_supports(int T, int dk, int dv, int dt);
+hipError_t launch_short_bf16(const void* q, const void* k, const void* v, const float* state_in, float* state_out,
+                             void* y, int B, int H, int T, int dk, int dv, const HeadGroup& g, hipStream_t s);
+
 // Copies state_in (or zeros when null) into state_out: the T = 0 case.
 hipError_t launch_state_copy(const float* state_in, float* state_out, size_t n, hipStream_t s);
 

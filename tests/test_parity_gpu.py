@@ -116,7 +116,7 @@ def test_chunkwise_vs_oracle(B, H, T, dk, dv, C, dt, with_state, gs):
     check("state_out", s, s_ref, bound)
 
 
-# ----------------------- short blocks (T <= 32): streaming kernels (fp32 MFMA / VALU)
+# ----------------------- short blocks (T <= 64): streaming kernels (bf16 MFMA / fp32 MFMA / VALU)
 SHORT_CASES = [
     # B, H, T, dk, dv, dtype, state_in, state_out ("new" / "inplace" / None), gammas
     (2, 3, 1, 64, 128, "f32", True, "new", [0.0, 0.9, 1.0]),
@@ -137,12 +137,21 @@ SHORT_CASES = [
     (2, 2, 32, 256, 512, "bf16", True, "inplace", [0.99, 1.0]),
     (1, 3, 25, 128, 128, "f32", False, "new", [0.5, 0.8, 0.999]),
     (1, 2, 29, 48, 192, "bf16", True, None, [0.95, 0.6]),
+    # bf16 blocks of up to 64 tokens with dk % 32 == 0 (bf16 MFMA streaming kernel)
+    (1, 2, 33, 256, 512, "bf16", True, "new", [0.99, 0.9]),
+    (2, 3, 48, 128, 192, "bf16", False, "new", [0.0, 0.8, 1.0]),
+    (1, 2, 64, 256, 512, "bf16", True, "inplace", [0.97, 0.999]),
+    (1, 2, 40, 64, 64, "bf16", True, None, [0.5, 0.95]),
+    (2, 2, 5, 32, 128, "bf16", True, "new", [0.9, 1.0]),
+    (1, 130, 21, 32, 64, "bf16", True, "inplace", None),
+    (1, 2, 57, 96, 320, "bf16", True, "new", [0.3, 0.99]),
 ]
 
 
 @pytest.mark.parametrize("B,H,T,dk,dv,dt,with_in,out,gs", SHORT_CASES)
 def test_short_block_vs_oracle(B, H, T, dk, dv, dt, with_in, out, gs):
-    """Blocks of at most 32 tokens take a one-pass streaming kernel (any C):
+    """Blocks of at most 64 tokens (bf16) or 32 tokens take a one-pass
+    streaming kernel (any C):
     y and the carried state against the oracle, with state_in absent or given,
     state_out absent, separate or the same buffer as state_in."""
     say(f"short block B{B} H{H} T{T} dk{dk} dv{dv} {dt} state_in={with_in} state_out={out}")
