@@ -75,6 +75,29 @@ def load_traffic(name, kernel_src):
         return None
 
 
+def load_mfma_counters(name, kernel_src):
+    """Executed bf16 MFMA share and MFMA-busy share of a kernel from a committed
+    rocprofv3 counter summary (SQ_INSTS_VALU_MFMA_MOPS_BF16,
+    SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE), if it was taken on the current
+    kernel source; else None."""
+    from retnet_retention_chunkwise_amd.rocprof_summary import read_traffic_file
+
+    p = os.path.join(PROFILES, name)
+    if not os.path.exists(p):
+        return None
+    rec = read_traffic_file(p)
+    if rec.get("kernel_source_sha256_16") != source_digest(kernel_src):
+        return None
+    try:
+        frac_key = next(k for k in rec if k.startswith("executed_mfma_frac"))
+        return {"profile": name, "kernel": rec["kernel"],
+                "executed_mfma_frac": float(rec[frac_key]),
+                "executed_bf16_mfma_tflops": float(rec["executed_bf16_mfma_tflops"].split()[0]),
+                "mfma_busy_frac": float(rec["mfma_busy_frac"].split()[0])}
+    except (KeyError, ValueError, StopIteration):
+        return None
+
+
 def host_cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -214,6 +237,7 @@ def bench_chunkwise(key, dev, steps, warmup, n_rot):
     gbs = alg_bytes / (ms * 1e-3) / 1e9
     tflops = alg_flops / (ms * 1e-3) / 1e12
     traffic = load_traffic(CHUNKWISE_TRAFFIC[key], os.path.join(CSRC, "chunkwise_mfma.hip"))
+    counters = load_mfma_counters(f"chunkwise_fwd_{key}_mfma_counters.txt", os.path.join(CSRC, "chunkwise_mfma.hip"))
     segs = "one launch" if not need else "state-only pass + segment scan + full pass (one call)"
     del sets, y, st, ws
     torch.cuda.empty_cache()
@@ -231,6 +255,7 @@ def bench_chunkwise(key, dev, steps, warmup, n_rot):
             "kernel_us": ms * 1e3, "kernel_us_event_pairs": ms_pairs * 1e3,
             "algorithmic_bytes_per_launch": alg_bytes, "algorithmic_flops_per_launch": alg_flops,
             "mfma_tflops": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS,
+            "mfma_counters": counters,
         },
     }
 

@@ -130,7 +130,7 @@ def _per_dispatch_all(directory: str):
     return acc, names
 
 
-def mfma(pmc_dir, stats_csv, kernel, cmd="", peak_tflops=2500.0, xcds=8, simds=1024):
+def mfma(pmc_dir, stats_csv, kernel, cmd="", peak_tflops=2500.0, xcds=8, simds=1024, source=None):
     """MFMA work and busy share of one kernel from a counter run (and its
     steady-state duration from a kernel-trace stats file)."""
     files = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
@@ -164,8 +164,11 @@ def mfma(pmc_dir, stats_csv, kernel, cmd="", peak_tflops=2500.0, xcds=8, simds=1
     lines = []
     if cmd:
         lines.append(f"command: {cmd}")
+    lines.append(f"kernel: {kernel}")
+    if source:
+        lines += [f"kernel_source: {os.path.basename(source)}",
+                  f"kernel_source_sha256_16: {hashlib.sha256(open(source, 'rb').read()).hexdigest()[:16]}"]
     lines += [
-        f"kernel: {kernel}",
         f"dispatches_averaged: {len(keys)} (counters), {calls} (trace)",
         f"SQ_INSTS_VALU_MFMA_MOPS_BF16_per_launch: {mops:.0f}",
         f"SQ_VALU_MFMA_BUSY_CYCLES_per_launch: {busy:.0f}",
@@ -208,12 +211,13 @@ def main(argv=None):
     m.add_argument("--pmc", required=True)
     m.add_argument("--stats", required=True)
     m.add_argument("--kernel", required=True)
+    m.add_argument("--source", default=None)
     m.add_argument("--cmd", default="")
     a = ap.parse_args(argv)
     if a.cmd_name == "stats":
         sys.stdout.write(stats_table(a.csv, a.cmd))
     elif a.cmd_name == "mfma":
-        sys.stdout.write(mfma(a.pmc, a.stats, a.kernel, a.cmd))
+        sys.stdout.write(mfma(a.pmc, a.stats, a.kernel, a.cmd, source=a.source))
     else:
         sys.stdout.write(traffic(a.fetch, a.write, a.kernel, a.source, a.copy_mib, a.copy_kernel, a.cmd))
 
