@@ -239,6 +239,7 @@ def bench_chunkwise(key, dev, steps, warmup, n_rot):
     traffic = load_traffic(CHUNKWISE_TRAFFIC[key], os.path.join(CSRC, "chunkwise_mfma.hip"))
     counters = load_mfma_counters(f"chunkwise_fwd_{key}_mfma_counters.txt", os.path.join(CSRC, "chunkwise_mfma.hip"))
     segs = "one launch" if not need else "state-only pass + segment scan + full pass (one call)"
+    gn = bench_fused_group_norm(wl, sets, y, st, ws, steps, warmup, stream, ms, alg_bytes)
     del sets, y, st, ws
     torch.cuda.empty_cache()
     return {
@@ -257,6 +258,55 @@ def bench_chunkwise(key, dev, steps, warmup, n_rot):
             "mfma_tflops": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS,
             "mfma_counters": counters,
         },
+        "group_norm_fused": gn,
+    }
+
+
+def bench_fused_group_norm(wl, sets, y, st, ws, steps, warmup, stream, ms_fwd, fwd_bytes):
+    """The same workload with the per-head GroupNorm (affine) of its output:
+    the fused call (retention_chunkwise_fwd_group_norm) against the forward
+    followed by retention_group_norm in place, both as graph replays over the
+    same rotating input sets."""
+    import torch
+
+    import retnet_retention_chunkwise_amd as ret
+
+    gen = torch.Generator().manual_seed(7)
+    w = torch.randn(wl.H, wl.dv, generator=gen).to(y.device)
+    b = torch.randn(wl.H, wl.dv, generator=gen).to(y.device)
+    lib = ret.load()
+    need = int(lib.retention_chunkwise_fwd_group_norm_workspace_bytes(wl.B, wl.H, wl.T, wl.dk, wl.dv, wl.C, 1))
+    wsf = torch.empty(max(need, 16), dtype=torch.uint8, device=y.device)
+    g = list(wl.gammas)
+    n_rot = len(sets)
+
+    def fused(i):
+        qd, kd, vd = sets[i % n_rot]
+        ret.chunkwise_fwd_group_norm(qd, kd, vd, g, wl.C, w, b, 1e-5, y=y, state_out=st, workspace=wsf)
+
+    def separate(i):
+        qd, kd, vd = sets[i % n_rot]
+        ret.chunkwise_fwd(qd, kd, vd, g, wl.C, y=y, state_out=st, workspace=ws)
+        ret.group_norm(y, w, b, 1e-5, out=y)
+
+    for i in range(warmup):
+        fused(i)
+    torch.cuda.synchronize()
+    ms_fused = graph_time_ms(fused, steps, stream)
+    err = int(wsf[:4].view(torch.int32).item())
+    for i in range(warmup // 4):
+        separate(i)
+    torch.cuda.synchronize()
+    ms_sep = graph_time_ms(separate, steps, stream)
+    alg = fwd_bytes + 2 * wl.H * wl.dv * 4
+    gbs = alg / (ms_fused * 1e-3) / 1e9
+    return {
+        "workload": "the same call with the per-head GroupNorm (affine weight and bias, eps 1e-5) of its output",
+        "fused_us": ms_fused * 1e3, "forward_then_group_norm_us": ms_sep * 1e3, "forward_alone_us": ms_fwd * 1e3,
+        "fused_extra_us": (ms_fused - ms_fwd) * 1e3, "separate_extra_us": (ms_sep - ms_fwd) * 1e3,
+        "wait_gave_up": err,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes_per_launch": alg},
     }
 
 
@@ -482,7 +532,7 @@ def main():
     if want("group_norm"):
         res["group_norm"] = bench_group_norm(dev)
     if cpu:
-        samples = {"long64k": (1, 4096), "layer6p7b": (1, 1024), "layer1p3b": (4, 2048)}
+        samples = {"long64k": (1, 65536), "layer6p7b": (1, 8192), "layer1p3b": (4, 2048)}
         for key, (sb, stt) in samples.items():
             if key in res:
                 res[key]["cpu_baseline"] = cpu_baseline_chunkwise(WORKLOADS[key], sb, stt)

@@ -201,6 +201,45 @@ ret_status retention_group_norm(const void* y, const float* weight, const float*
                                 int H, int T, int dv, ret_dtype dt, void* stream);
 
 /*
+ * The chunkwise forward followed by the per-head GroupNorm of its output, in
+ * one pass: y receives retention_group_norm(retention_chunkwise_fwd(...)) and
+ * the un-normalised output is never written to memory.  The paperhub page
+ * (author answer A4) names GroupNorm per head as the normalisation of
+ * multi-scale retention; the closing list there names retention and group
+ * normalization together.  Arguments are those of retention_chunkwise_fwd
+ * plus weight, bias and eps of retention_group_norm (weight/bias nullable,
+ * device fp32 [H,dv]; eps finite, >= 0); state_out receives the carried state
+ * as there.  The outputs are rounded to dt before they are normalised, as the
+ * two separate calls do; the statistics are fp32.
+ * bf16 calls on the bf16 MFMA kernel (dk in {64,128,256}, dv % 64 == 0,
+ * dv <= 512, T > 64) normalise inside that kernel: the dv/64 column-tile
+ * workgroups of a head exchange per-row partial statistics through the
+ * workspace.  Every other call runs the forward and then
+ * retention_group_norm on y in place.
+ *   workspace : at least retention_chunkwise_fwd_group_norm_workspace_bytes()
+ *               bytes (may be NULL when that is 0), 16-byte aligned, owned by
+ *               the caller, overlapping no other argument.  For the fused
+ *               kernel its first 32-bit word is 0 after the call, or 1 if a
+ *               workgroup gave up waiting for another tile's statistics
+ *               (possible only if the tiles of a head cannot all be resident
+ *               on the device at once; y is then wrong).
+ * Errors as retention_chunkwise_fwd; y must not overlap weight or bias.
+ */
+ret_status retention_chunkwise_fwd_group_norm(const void* q, const void* k, const void* v, const float* gamma,
+                                              const float* state_in, float* state_out, const float* weight,
+                                              const float* bias, float eps, void* y, int B, int H, int T, int dk,
+                                              int dv, int C, ret_dtype dt, void* workspace, size_t workspace_bytes,
+                                              void* stream);
+
+/* Workspace size for retention_chunkwise_fwd_group_norm (0 when the call
+ * needs none).  Fused calls: 256 bytes + the segment slots of
+ * retention_chunkwise_workspace_bytes (rounded up to 256 bytes) + 8 bytes per
+ * row and column tile, nseg * B * H * (dv/64) * seg_len * 8, where seg_len is
+ * the segment length (T without segments).  Other calls: the forward's
+ * workspace.  Returns (size_t)-1 for arguments the call would reject. */
+size_t retention_chunkwise_fwd_group_norm_workspace_bytes(int B, int H, int T, int dk, int dv, int C, ret_dtype dt);
+
+/*
  * One recurrent (decode) step, in place on the state: S <- gamma S + k^T v,
  * then y = q S (the new state, so the current token is included).  This is the
  * recurrent form of the aimpact page ("Il meccanismo"); the baulab page

@@ -11,6 +11,8 @@ The compute lives in hand-written HIP kernels behind a C ABI
     parallel_fwd(q, k, v, gamma, state_in=None) -> y
     recurrent_step(q, k, v, gamma, state) -> y          (state updated in place)
     group_norm(y, weight=None, bias=None, eps=1e-5) -> out   (per-head GroupNorm of y)
+    chunkwise_fwd_group_norm(q, k, v, gamma, C, weight=None, bias=None, eps=1e-5, ...)
+        -> (y, state_out)     (the forward with the GroupNorm fused into its stores)
 
 Build the library with ``python -m retnet_retention_chunkwise_amd.build``.
 """
@@ -22,6 +24,7 @@ from ._lib import (  # noqa: F401
     RetentionError,
     chunkwise_bwd,
     chunkwise_fwd,
+    chunkwise_fwd_group_norm,
     chunkwise_fwd_noalloc,
     chunkwise_workspace_bytes,
     group_norm,

@@ -27,6 +27,9 @@ SIGNATURES = {
     "retention_parallel_fwd": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "retention_chunkwise_fwd": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "retention_chunkwise_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "retention_chunkwise_fwd_group_norm": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _i, _i,
+                                                _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "retention_chunkwise_fwd_group_norm_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "retention_chunkwise_fwd_noalloc": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "retention_recurrent_step": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "retention_group_norm": (_i, [_vp, _vp, _vp, ctypes.c_float, _vp, _i, _i, _i, _i, _i, _vp]),
@@ -200,6 +203,49 @@ def chunkwise_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma, C: i
                                      _ptr(state_out), _ptr(y), B, H, T, dk, dv, int(C), dt, _ptr(workspace),
                                      ws_bytes, _stream(q.device))
     _check(st)
+    return y, state_out
+
+
+def chunkwise_fwd_group_norm(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma, C: int,
+                             weight: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                             eps: float = 1e-5, state_in: Optional[torch.Tensor] = None,
+                             state_out: Union[torch.Tensor, bool, None] = True, y: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None
+                             ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """The chunkwise forward with the per-head GroupNorm of its output fused in
+    (retention_chunkwise_fwd_group_norm): y = group_norm(chunkwise_fwd(...)).
+    weight, bias: optional fp32 [H,dv].  Returns (y, state_out)."""
+    lib = load()
+    B, H, T, dk, dv, dt = _qkv_shapes(q, k, v)
+    if y is not None:
+        _out_check(y, (B, H, T, dv), q.dtype, q.device, "y")
+    _qkv_devices(q, k, v)
+    sshape = (B, H, dk, dv)
+    _state_check(state_in, sshape, q.device, "state_in")
+    if state_out is True:
+        state_out = torch.empty(sshape, dtype=torch.float32, device=q.device)
+    elif state_out is False:
+        state_out = None
+    _state_check(state_out, sshape, q.device, "state_out")
+    for t, n in ((weight, "weight"), (bias, "bias")):
+        if t is not None:
+            _dev(t, n)
+            if t.dtype != torch.float32 or tuple(t.shape) != (H, dv) or t.device != q.device:
+                raise ValueError(f"{n} must be float32 ({H}, {dv}) on {q.device}")
+    if y is None:
+        y = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    need = int(lib.retention_chunkwise_fwd_group_norm_workspace_bytes(B, H, T, dk, dv, int(C), dt))
+    ws_bytes = 0
+    if need and need != ctypes.c_size_t(-1).value:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    elif workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.retention_chunkwise_fwd_group_norm(_ptr(q), _ptr(k), _ptr(v), _gamma_array(gamma, H), _ptr(state_in),
+                                                  _ptr(state_out), _ptr(weight), _ptr(bias), float(eps), _ptr(y), B,
+                                                  H, T, dk, dv, int(C), dt, _ptr(workspace), ws_bytes,
+                                                  _stream(q.device)))
     return y, state_out
 
 

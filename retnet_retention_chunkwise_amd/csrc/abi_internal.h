@@ -22,9 +22,9 @@ struct ChunkwiseFwdArgs {
 
 // Every argument check of retention_chunkwise_fwd; the workspace (pointer,
 // size, alignment, overlaps) only when check_ws.  Makes no HIP call; sets the
-// error text on failure.
+// error text (naming the entry point fn) on failure.
 ret_status chunkwise_fwd_check(const ChunkwiseFwdArgs& a, const void* workspace, size_t workspace_bytes,
-                               bool check_ws);
+                               bool check_ws, const char* fn);
 
 // Kernel choice and launch of a checked call; workspace holds
 // retention_chunkwise_workspace_bytes() bytes when that is non-zero.

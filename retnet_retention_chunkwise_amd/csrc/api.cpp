@@ -99,8 +99,7 @@ void set_last_error(const char* text) { g_last_error = text; }
 // Validation of a chunkwise forward call: sizes, pointers, aliasing and (when
 // check_ws) the caller's workspace.  Makes no HIP call.
 ret_status chunkwise_fwd_check(const ChunkwiseFwdArgs& a, const void* workspace, size_t workspace_bytes,
-                               bool check_ws) {
-  const char* fn = check_ws ? "retention_chunkwise_fwd" : "retention_chunkwise_fwd_noalloc";
+                               bool check_ws, const char* fn) {
   const int B = a.B, H = a.H, T = a.T, dk = a.dk, dv = a.dv, C = a.C;
   const ret_dtype dt = static_cast<ret_dtype>(a.dt);
   ret_status st = check_common(fn, B, H, T, dk, dv, dt, a.gamma);
@@ -188,6 +187,20 @@ ret_status chunkwise_fwd_run(const ChunkwiseFwdArgs& a, void* workspace, void* s
   });
 }
 
+// The fused GroupNorm runs inside the bf16 MFMA kernel.  Calls that take
+// another kernel (blocks of up to 64 tokens, fp32, other shapes) run the
+// forward and then the standalone GroupNorm on y in place.
+bool gn_fused(int B, int H, int T, int dk, int dv, int C, int dt) {
+  return T > kShortBf16MaxT && chunkwise_mfma_supports(T, dk, dv, C, dt) && chunkwise_gn_supports(B, H, T, dv, C);
+}
+
+// Workspace of the fused call: [error word | 256 B][segment slots][records].
+constexpr size_t kGnHead = 256;
+size_t gn_slot_bytes(int B, int H, int T, int dk, int dv, int C) {
+  const size_t b = chunkwise_segment_slots(chunkwise_mfma_segments(B, H, T, dv, C)) * B * H * dk * dv * sizeof(float);
+  return (b + 255) / 256 * 256;
+}
+
 }  // namespace ret
 
 extern "C" {
@@ -258,9 +271,70 @@ ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, 
                                    int dv, int C, ret_dtype dt, void* workspace, size_t workspace_bytes,
                                    void* stream) {
   const ret::ChunkwiseFwdArgs a{q, k, v, gamma, state_in, state_out, y, B, H, T, dk, dv, C, static_cast<int>(dt)};
-  const ret_status st = ret::chunkwise_fwd_check(a, workspace, workspace_bytes, true);
+  const ret_status st = ret::chunkwise_fwd_check(a, workspace, workspace_bytes, true, "retention_chunkwise_fwd");
   if (st != RET_OK) return st;
   return ret::chunkwise_fwd_run(a, workspace, stream);
+}
+
+size_t retention_chunkwise_fwd_group_norm_workspace_bytes(int B, int H, int T, int dk, int dv, int C, ret_dtype dt) {
+  const size_t fwd = retention_chunkwise_workspace_bytes(B, H, T, dk, dv, C, dt);
+  if (fwd == static_cast<size_t>(-1)) return fwd;
+  if (!ret::gn_fused(B, H, T, dk, dv, C, static_cast<int>(dt))) return fwd;
+  return ret::kGnHead + ret::gn_slot_bytes(B, H, T, dk, dv, C) + ret::chunkwise_gn_record_bytes(B, H, T, dv, C);
+}
+
+ret_status retention_chunkwise_fwd_group_norm(const void* q, const void* k, const void* v, const float* gamma,
+                                              const float* state_in, float* state_out, const float* weight,
+                                              const float* bias, float eps, void* y, int B, int H, int T, int dk,
+                                              int dv, int C, ret_dtype dt, void* workspace, size_t workspace_bytes,
+                                              void* stream) {
+  const char* fn = "retention_chunkwise_fwd_group_norm";
+  const ret::ChunkwiseFwdArgs a{q, k, v, gamma, state_in, state_out, y, B, H, T, dk, dv, C, static_cast<int>(dt)};
+  ret_status st = ret::chunkwise_fwd_check(a, nullptr, 0, false, fn);
+  if (st != RET_OK) return st;
+  if (!std::isfinite(eps) || eps < 0.0f)
+    return fail(RET_ERR_INVALID_ARG, "%s: eps = %g must be finite and >= 0", fn, static_cast<double>(eps));
+  if (misaligned(weight) || misaligned(bias) || misaligned(workspace))
+    return fail(RET_ERR_UNSUPPORTED, "%s: tensor pointers must be 16-byte aligned", fn);
+  const size_t es = dsize(dt);
+  const size_t bht = static_cast<size_t>(B) * H * T;
+  const size_t ny = bht * dv * es, nk = bht * dk * es;
+  const size_t ns = static_cast<size_t>(B) * H * dk * dv * 4;
+  const size_t nw = static_cast<size_t>(H) * dv * 4;
+  if (overlap(y, ny, weight, nw) || overlap(y, ny, bias, nw))
+    return fail(RET_ERR_INVALID_ARG, "%s: y overlaps weight or bias", fn);
+  if (state_out != nullptr && (overlap(state_out, ns, weight, nw) || overlap(state_out, ns, bias, nw)))
+    return fail(RET_ERR_INVALID_ARG, "%s: state_out overlaps weight or bias", fn);
+  const size_t need = retention_chunkwise_fwd_group_norm_workspace_bytes(B, H, T, dk, dv, C, dt);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(RET_ERR_INVALID_ARG, "%s: workspace of %zu bytes required, %zu given", fn, need, workspace_bytes);
+  if (need > 0 && (overlap(workspace, need, y, ny) || overlap(workspace, need, q, nk) ||
+                   overlap(workspace, need, k, nk) || overlap(workspace, need, v, ny) ||
+                   overlap(workspace, need, state_in, ns) || overlap(workspace, need, state_out, ns) ||
+                   overlap(workspace, need, weight, nw) || overlap(workspace, need, bias, nw)))
+    return fail(RET_ERR_INVALID_ARG, "%s: workspace overlaps another argument", fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!ret::gn_fused(B, H, T, dk, dv, C, static_cast<int>(dt))) {
+    st = ret::chunkwise_fwd_run(a, workspace, stream);
+    if (st != RET_OK || T == 0) return st;
+    const hipError_t e = ret::launch_group_norm(y, weight, bias, eps, y, B, H, T, dv, static_cast<int>(dt), s);
+    return e == hipSuccess ? ok() : hip_fail(fn, e);
+  }
+  char* base = static_cast<char*>(workspace);
+  int* err = reinterpret_cast<int*>(base);
+  float* slots = reinterpret_cast<float*>(base + ret::kGnHead);
+  void* records = base + ret::kGnHead + ret::gn_slot_bytes(B, H, T, dk, dv, C);
+  const size_t rec_bytes = ret::chunkwise_gn_record_bytes(B, H, T, dv, C);
+  hipError_t e = ret::launch_fill_u32(err, 1, 0u, s);
+  if (e == hipSuccess) e = ret::launch_fill_u32(records, rec_bytes / 4, 0xFFFFFFFFu, s);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  const ret::ChunkSegments segs = ret::chunkwise_mfma_segments(B, H, T, dv, C);
+  // a wait for another tile's records gives up after 2^16 device-scope polls
+  // (about 0.1 s), sets the error word and goes on
+  const ret::GnLaunch gl{weight, bias, eps, records, err, 1 << 16};
+  return for_head_groups(fn, H, gamma, [&](const ret::HeadGroup& g) {
+    return ret::launch_chunkwise_mfma_gn(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, segs, slots, gl, g, s);
+  });
 }
 
 size_t retention_chunkwise_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C, ret_dtype dt) {

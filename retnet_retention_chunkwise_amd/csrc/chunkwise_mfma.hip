@@ -96,6 +96,32 @@ struct PassPtrs {
   float* ws;       // segment slots (nseg > 1) or null
 };
 
+// Per-head GroupNorm fused into the output stores (kGN), the normalisation of
+// multi-scale retention (paperhub page, author answer A4: GroupNorm, one group
+// per head).  A head's dv outputs of a token are spread over its dv/64
+// column-tile workgroups, so each output wave publishes, per token row of its
+// query blocks, one 64-bit record: the mean and the sum of squared deviations
+// of its tile's 64 rounded outputs.  Records sit at
+// rec[segment][batch][head][tile][position in the segment], are filled with
+// the all-ones sentinel before the launch (no arithmetic result has that bit
+// pattern) and are valid once they differ from it.  A chunk's rounded outputs
+// wait GD chunks (in registers or LDS) for the other tiles' records; the tiles
+// then combine the records of a row (parallel-variance formula) and store the
+// normalised outputs.  The un-normalised outputs never reach memory.
+struct GnArgs {
+  const float* weight;      // [H_total, dv] or null (ones)
+  const float* bias;        // [H_total, dv] or null (zeros)
+  float eps;
+  unsigned long long* rec;  // records (see above)
+  int* err;                 // set to 1 if a wait gave up (spin_limit)
+  int B;
+  int Htot;
+  int spin_limit;
+  int items;  // work items of the launch; the grid may be padded past them
+};
+constexpr unsigned long long kGnEmpty = ~0ull;
+constexpr int kGnDelay = 2;  // chunks a rounded output waits for the records
+
 // kOut = true: the full kernel (outputs and state, 4 + 4 waves).
 // kOut = false: the state-only pass, end states from zero of the segments (or
 // sub-segments) given by sg (4 state waves; at d_k <= 256 three of its
@@ -122,11 +148,12 @@ struct PassPtrs {
 // for launches that run one or two passes of either direction (dQ forward,
 // dK and dV reverse).
 
-template <int CT, int DK, bool kOut, bool kZS, int kDir>
+template <int CT, int DK, bool kOut, bool kZS, int kDir, bool kGN = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kOut ? 512 : 256, kOut ? 512 : 256),
                           amdgpu_waves_per_eu(kOut ? 2 : (DK <= 256 ? 3 : 1), kOut ? 2 : 4))) void
 chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H, int h0, int nh, int Tn, int dv,
-                      int C, int ntiles, SegArgs sg) {
+                      int C, int ntiles, SegArgs sg, GnArgs gn) {
+  static_assert(!kGN || (kOut && kDir == 0), "the fused GroupNorm is a forward epilogue");
   using F = Cfg<CT, DK, kOut>;
   constexpr int NSP = CT / 32;  // key (token) steps of 32 per chunk tile
   constexpr int NB = F::NBUF;
@@ -137,6 +164,15 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
   // with two copies zeta is applied to the update's V operand in registers.
   constexpr bool kVz = NB == 1 && !kZS;
   __shared__ __attribute__((aligned(16))) uint16_t Vz[kVz ? CT * F::VLD : 8];
+  // Fused GroupNorm: the tile's 64 weights and biases, and with 128-token
+  // tiles the rounded outputs waiting for the records (kGnHold chunks of 4
+  // waves x 2 query blocks x 4 column blocks x 64 lanes x 8 bytes; two when
+  // they fit the LDS beside the K, V and R^T tiles).
+  constexpr int kLdsBase = 2 * (NB * CT * F::KLD + NB * CT * F::VLD + NB * kTN * F::RLD + (kVz ? CT * F::VLD : 0));
+  constexpr bool kGnLds = kGN && F::NQ == 2;
+  constexpr int kGnHold = !kGN ? 1 : !kGnLds ? kGnDelay : (kLdsBase + 2 * 16384 + 512 <= 160 * 1024 ? 2 : 1);
+  __shared__ __attribute__((aligned(16))) float Gwb[kGN ? 2 * kTN : 4];
+  __shared__ __attribute__((aligned(16))) u32x2 Gh[kGnLds ? kGnHold * 4 * 2 * 4 * 64 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -152,6 +188,7 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
   const int total = gridDim.x;
   int lin = blockIdx.x;
   if ((total & 7) == 0) lin = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  if (kGN && lin >= gn.items) return;  // padding of a fused-GroupNorm grid (before any barrier)
   const int tile = lin % ntiles;
   const int pz = npass > 1 ? (lin / ntiles) % npass : 0;
   const int bh = (lin / ntiles / npass) % sg.bnh;
@@ -528,11 +565,140 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
         for (int s = 0; s < F::KS; ++s) Qd[qi][s] = __builtin_bit_cast(bf16x8, buffer_load16(rq, rowoff + 64u * s));
       }
     };
+
+    // ---- fused GroupNorm (kGN) ----
+    // Lane (g, c16) holds row c16 of each query block; it reads the records of
+    // tiles g and g+4 for those rows.  The records of chunk ci - GD are loaded
+    // at the start of chunk ci, before the chunk's Q prefetch, so that waiting
+    // for them at its end does not wait for that prefetch; no load or store of
+    // this path sits in a branch of the common case (rows past the chunk,
+    // tiles past ntiles and chunks before the first get an offset past the
+    // buffer: reads give 0, writes are dropped), so the compiler's wait counts
+    // stay exact.  The first read of a record is a workgroup-scope load: the
+    // tiles of a head share an XCD (the host pads the grid to a multiple of 8
+    // tiles per head and workgroups go round-robin over the 8 XCDs), so it
+    // finds the line in that L2.  A record seen as the sentinel is read again
+    // with device-scope loads (which see the writer's device-scope store)
+    // until it is valid or spin_limit polls have passed.
+    constexpr int GQ = kGN ? F::NQ : 1;
+    constexpr int GD = kGnHold;
+    static_assert(!kGN || kGnLds || GD == 2, "register holds alternate two slots");
+    typedef u32x2 Held[GQ][4];
+    Held held[kGN && !kGnLds ? GD : 1];
+    unsigned long long grec[GQ][2];
+    constexpr uint32_t kOutside = 0x80000000u;
+    rsrc_t rrs = make_rsrc(nullptr, 0u);
+    if constexpr (kGN) {
+#pragma unroll
+      for (int d = 0; d < (kGnLds ? 1 : GD); ++d)
+#pragma unroll
+        for (int qi = 0; qi < GQ; ++qi)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) held[d][qi][nb] = u32x2{0u, 0u};
+      const long item = (static_cast<long>(seg) * gn.B + b) * gn.Htot + h0 + hl;
+      rrs = make_rsrc(gn.rec + item * ntiles * static_cast<long>(sg.seg_len),
+                      static_cast<uint32_t>(ntiles) * static_cast<uint32_t>(sg.seg_len) * 8u);
+      if constexpr (W == 0) {
+        // the tile's weights and biases (null: ones and zeros)
+        const long hoff = static_cast<long>(h0 + hl) * dv + col0;
+        Gwb[lane] = gn.weight != nullptr ? gn.weight[hoff + lane] : 1.0f;
+        Gwb[kTN + lane] = gn.bias != nullptr ? gn.bias[hoff + lane] : 0.0f;
+      }
+    }
+    auto row_of = [&](int qi) __attribute__((always_inline)) { return 16 * (qi == 0 ? W : QB1) + c16; };
+    auto chunk_len = [&](int cj) __attribute__((always_inline)) {
+      return cj >= 0 ? min(C, t_end - (t_begin + cj * C)) : 0;
+    };
+    auto rec_off = [&](int t, int cj, int qi) __attribute__((always_inline)) -> uint32_t {
+      return row_of(qi) < chunk_len(cj) && t < ntiles
+                 ? static_cast<uint32_t>(t * sg.seg_len + cj * C + row_of(qi)) * 8u
+                 : kOutside;
+    };
+    using kFirst = std::integral_constant<bool, true>;
+    using kRetry = std::integral_constant<bool, false>;
+    auto gn_load = [&](int cj, auto first_c) __attribute__((always_inline)) {
+      constexpr int aux = decltype(first_c)::value ? 1 : 16;  // sc0 : sc1
+#pragma unroll
+      for (int qi = 0; qi < GQ; ++qi)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          grec[qi][i] = __builtin_bit_cast(unsigned long long,
+                                           __builtin_amdgcn_raw_buffer_load_b64(rrs, rec_off(g + 4 * i, cj, qi), 0, aux));
+    };
+    auto gn_valid = [&]() __attribute__((always_inline)) {
+      bool ok = true;
+#pragma unroll
+      for (int qi = 0; qi < GQ; ++qi)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) ok = ok && grec[qi][i] != kGnEmpty;
+      return __all(ok) != 0;
+    };
+    // combine the records of chunk cj, normalise its held outputs and store them
+    auto gn_finish = [&](int cj, auto hold) __attribute__((always_inline)) {
+      if (__builtin_expect(!gn_valid(), 0)) {
+        int spin = 0;
+        bool ok;
+        do {
+          __builtin_amdgcn_s_sleep(2);
+          gn_load(cj, kRetry());
+          ok = gn_valid();
+        } while (!ok && ++spin < gn.spin_limit);
+        // the error word (device scope), written by lane 0 of a wave that gave up
+        if (!ok) __builtin_amdgcn_raw_buffer_store_b32(1, make_rsrc(gn.err, 4u), lane == 0 ? 0u : kOutside, 0, 16);
+      }
+      const int L = chunk_len(cj);
+      const rsrc_t ry = make_rsrc(yh + static_cast<long>(L > 0 ? first_row(t_begin + cj * C, L) : 0) * dv,
+                                  L > 0 ? static_cast<uint32_t>(L - 1) * vrow + kTN * 2u : 0u);
+      const float inv_t = 1.0f / static_cast<float>(ntiles);
+      const float inv_n = 1.0f / static_cast<float>(dv);
+#pragma unroll
+      for (int qi = 0; qi < GQ; ++qi) {
+        float m[2], q[2];
+        bool in[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          in[i] = g + 4 * i < ntiles;
+          m[i] = __uint_as_float(static_cast<uint32_t>(grec[qi][i]));
+          q[i] = __uint_as_float(static_cast<uint32_t>(grec[qi][i] >> 32));
+        }
+        // mean of the tile means (every tile holds 64 columns), then the sum
+        // of squared deviations: sum_t (M2_t + 64 (mean_t - mean)^2)
+        float ms = (in[0] ? m[0] : 0.0f) + (in[1] ? m[1] : 0.0f);
+        ms = row4_sum(ms);
+        const float mean = ms * inv_t;
+        float qs = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const float d = m[i] - mean;
+          qs += in[i] ? fmaf(static_cast<float>(kTN) * d, d, q[i]) : 0.0f;
+        }
+        qs = row4_sum(qs);
+        const float rstd = 1.0f / sqrtf(qs * inv_n + gn.eps);
+        const uint32_t roff = row_off(row_of(qi), L, vrow) + 8u * g;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const f32x4 x = __builtin_convertvector(__builtin_bit_cast(bf16x4, hold(qi, nb)), f32x4);
+          const f32x4 wv = *reinterpret_cast<const f32x4*>(&Gwb[16 * nb + 4 * g]);
+          const f32x4 bv = *reinterpret_cast<const f32x4*>(&Gwb[kTN + 16 * nb + 4 * g]);
+          f32x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = fmaf((x[e] - mean) * rstd, wv[e], bv[e]);
+          buffer_store8(ry, roff + 32u * nb, __builtin_bit_cast(u32x2, __builtin_convertvector(o, bf16x4)));
+        }
+      }
+    };
+    // LDS hold slot of chunk cj (128-token tiles), this lane's entry
+    auto gh_at = [&](int cj, int qi, int nb) __attribute__((always_inline)) -> u32x2& {
+      return Gh[(((cj % GD) * 4 + W) * 2 * 4 + qi * 4 + nb) * 64 + lane];
+    };
+
     load_q(Qa, t_begin, min(C, t_end - t_begin));
     lds_barrier();  // chunk 0 staged, R_0 published
 
-    // one chunk with Q in Qreg; Qnext receives the next chunk's Q (kQ2)
-    auto chunk = [&](int ci, QTile& Qreg, QTile& Qnext) __attribute__((always_inline)) {
+    // one chunk with Q in Qreg; Qnext receives the next chunk's Q (kQ2);
+    // slot_c: register hold slot of the chunk (fused GroupNorm)
+    auto chunk = [&](int ci, QTile& Qreg, QTile& Qnext, auto slot_c) __attribute__((always_inline)) {
+      constexpr int slot = decltype(slot_c)::value;
       const int s0 = t_begin + ci * C;
       const int L = min(C, t_end - s0);
       const int s1 = s0 + C;
@@ -541,6 +707,7 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
       const uint16_t* Kx = Ks[X];
       const uint16_t* Vx = Vs[X];
       const uint16_t* Rx = Rt[X];
+      if constexpr (kGN) gn_load(ci - GD, kFirst());
       if constexpr (kQ2) load_q(Qnext, s1, Ln);
 
       // cross-chunk term O^T = (R_i^T Q^T) diag(gamma^(j+1)); V^T P^T
@@ -659,9 +826,69 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
       for (int sp = 0; sp < NSP; ++sp)
         if (2 * sp <= QMAX) pv(sp);
       if constexpr (NB == 1) lds_barrier();  // this chunk's K, V and R^T are no longer read
-      // store Y rows, 4 columns (8 bytes) per lane and block (rows past the
-      // chunk end fall outside the buffer and are dropped)
-      {
+      if constexpr (kGN) {
+        // round to the output dtype; this tile's record of each of the lane's
+        // rows: mean and sum of squared deviations over the tile's 64 columns
+        Held hn;
+        float gm[GQ], gq[GQ];
+#pragma unroll
+        for (int qi = 0; qi < GQ; ++qi) {
+          float x[16];
+          float sm = 0.0f;
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            const bf16x4 o = __builtin_convertvector(kZS ? O[qi][nb] * xi[qi] : O[qi][nb], bf16x4);
+            hn[qi][nb] = __builtin_bit_cast(u32x2, o);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[4 * nb + e] = static_cast<float>(o[e]);
+              sm += x[4 * nb + e];
+            }
+          }
+          sm = row4_sum(sm);
+          const float mt = sm * (1.0f / kTN);
+          float q2 = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const float d = x[j] - mt;
+            q2 = fmaf(d, d, q2);
+          }
+          q2 = row4_sum(q2);
+          gm[qi] = mt;
+          gq[qi] = q2;
+        }
+        // publish (lane group 0): a plain store, which the XCD's L2 holds for
+        // the first reads, and a device-scope store for the retries
+#pragma unroll
+        for (int qi = 0; qi < GQ; ++qi) {
+          const u32x2 r = {__float_as_uint(gm[qi]), __float_as_uint(gq[qi])};
+          const uint32_t off = g == 0 ? rec_off(tile, ci, qi) : kOutside;
+          __builtin_amdgcn_raw_buffer_store_b64(r, rrs, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(r, rrs, off, 0, 16);
+        }
+        // normalise chunk ci - GD (its records were loaded at the start of
+        // this chunk), then hold this chunk's outputs in the freed slot.  No
+        // instruction moves across this point: the records' validity check
+        // would otherwise be hoisted to the start of the chunk and wait there
+        // for loads issued just before.
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kGnLds) {
+          // (chunk ci - GD holds the slot that chunk ci takes)
+          gn_finish(ci - GD, [&](int qi, int nb) { return gh_at(ci, qi, nb); });
+#pragma unroll
+          for (int qi = 0; qi < GQ; ++qi)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) gh_at(ci, qi, nb) = hn[qi][nb];
+        } else {
+          gn_finish(ci - GD, [&](int qi, int nb) { return held[slot][qi][nb]; });
+#pragma unroll
+          for (int qi = 0; qi < GQ; ++qi)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) held[slot][qi][nb] = hn[qi][nb];
+        }
+      } else {
+        // store Y rows, 4 columns (8 bytes) per lane and block (rows past the
+        // chunk end fall outside the buffer and are dropped)
         const rsrc_t ry = make_rsrc(yh + static_cast<long>(first_row(s0, L)) * dv,
                                     static_cast<uint32_t>(L - 1) * vrow + kTN * 2u);
 #pragma unroll
@@ -676,13 +903,28 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
       }
       lds_barrier();  // the next chunk's R^T, K and V are in LDS
     };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
     for (int ci = 0; ci < nchunks; ci += 2) {
       if constexpr (kQ2) {
-        chunk(ci, Qa, Qb);
-        if (ci + 1 < nchunks) chunk(ci + 1, Qb, Qa);
+        chunk(ci, Qa, Qb, I0());
+        if (ci + 1 < nchunks) chunk(ci + 1, Qb, Qa, I1());
       } else {
-        chunk(ci, Qa, Qa);
-        if (ci + 1 < nchunks) chunk(ci + 1, Qa, Qa);
+        chunk(ci, Qa, Qa, I0());
+        if (ci + 1 < nchunks) chunk(ci + 1, Qa, Qa, I1());
+      }
+    }
+    if constexpr (kGN) {
+      // the chunks still waiting: nchunks - GD .. nchunks - 1
+      for (int cj = max(0, nchunks - GD); cj < nchunks; ++cj) {
+        gn_load(cj, kFirst());
+        if constexpr (kGnLds) {
+          gn_finish(cj, [&](int qi, int nb) { return gh_at(cj, qi, nb); });
+        } else if ((cj & 1) == 0) {
+          gn_finish(cj, [&](int qi, int nb) { return held[0][qi][nb]; });
+        } else {
+          gn_finish(cj, [&](int qi, int nb) { return held[1][qi][nb]; });
+        }
       }
     }
     };
@@ -733,9 +975,9 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ w
 // over the sub-segments of segments 0..nseg-2 (64-token chunks when the
 // sub-segment length allows, else the call's own tile and chunk), the scan of
 // every pass, then the full launch.
-template <int CT, int DK, bool kZS, int kDir>
+template <int CT, int DK, bool kZS, int kDir, bool kGN = false>
 hipError_t launch_cfg(const PassPtrs (&pp)[2], int npass, int B, int H, int Tn, int dx, int C, const HeadDecay& hd,
-                      const HeadGroup& g, const ChunkSegments& segs, hipStream_t s) {
+                      const HeadGroup& g, const ChunkSegments& segs, hipStream_t s, const GnArgs& gn = GnArgs{}) {
   const int ntiles = dx / kTN;
   const int bnh = B * g.nh;
   const long stride = static_cast<long>(B) * H * DK * dx;
@@ -750,10 +992,10 @@ hipError_t launch_cfg(const PassPtrs (&pp)[2], int npass, int B, int H, int Tn, 
     const SegArgs sp{sub_len, nsubs + 1, bnh, stride};
     if (sub_len % 64 == 0)
       hipLaunchKernelGGL((chunkwise_mfma_kernel<64, DK, false, kZS, kDir>), dim3(items * nsubs), dim3(256), 0, s,
-                         pre[0], pre[1], npass, hd, H, g.h0, g.nh, Tn, dx, 64, ntiles, sp);
+                         pre[0], pre[1], npass, hd, H, g.h0, g.nh, Tn, dx, 64, ntiles, sp, GnArgs{});
     else
       hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, false, kZS, kDir>), dim3(items * nsubs), dim3(256), 0, s,
-                         pre[0], pre[1], npass, hd, H, g.h0, g.nh, Tn, dx, C, ntiles, sp);
+                         pre[0], pre[1], npass, hd, H, g.h0, g.nh, Tn, dx, C, ntiles, sp, GnArgs{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long per_head = static_cast<long>(DK) * dx;
@@ -767,18 +1009,26 @@ hipError_t launch_cfg(const PassPtrs (&pp)[2], int npass, int B, int H, int Tn, 
     }
   }
   const SegArgs sg{segs.seg_len, segs.nseg, bnh, stride};
-  hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, true, kZS, kDir>), dim3(items * segs.nseg), dim3(512), 0, s, pp[0],
-                     pp[1], npass, hd, H, g.h0, g.nh, Tn, dx, C, ntiles, sg);
+  GnArgs ga = gn;
+  unsigned grid = static_cast<unsigned>(items * segs.nseg);
+  if (kGN) {
+    // a multiple of 8 * ntiles, so that the tiles of a head share an XCD
+    ga.items = static_cast<int>(grid);
+    const unsigned m = 8u * static_cast<unsigned>(ntiles);
+    grid = (grid + m - 1) / m * m;
+  }
+  hipLaunchKernelGGL((chunkwise_mfma_kernel<CT, DK, true, kZS, kDir, kGN>), dim3(grid), dim3(512), 0, s, pp[0], pp[1],
+                     npass, hd, H, g.h0, g.nh, Tn, dx, C, ntiles, sg, ga);
   return hipGetLastError();
 }
 
-template <int CT, bool kZS>
+template <int CT, bool kZS, bool kGN = false>
 hipError_t launch_fwd_ct(const PassPtrs (&pp)[2], int B, int H, int Tn, int dk, int dv, int C, const HeadDecay& hd,
-                         const HeadGroup& g, const ChunkSegments& segs, hipStream_t s) {
+                         const HeadGroup& g, const ChunkSegments& segs, hipStream_t s, const GnArgs& gn = GnArgs{}) {
   switch (dk) {
-    case 64: return launch_cfg<CT, 64, kZS, 0>(pp, 1, B, H, Tn, dv, C, hd, g, segs, s);
-    case 128: return launch_cfg<CT, 128, kZS, 0>(pp, 1, B, H, Tn, dv, C, hd, g, segs, s);
-    default: return launch_cfg<CT, 256, kZS, 0>(pp, 1, B, H, Tn, dv, C, hd, g, segs, s);
+    case 64: return launch_cfg<CT, 64, kZS, 0, kGN>(pp, 1, B, H, Tn, dv, C, hd, g, segs, s, gn);
+    case 128: return launch_cfg<CT, 128, kZS, 0, kGN>(pp, 1, B, H, Tn, dv, C, hd, g, segs, s, gn);
+    default: return launch_cfg<CT, 256, kZS, 0, kGN>(pp, 1, B, H, Tn, dv, C, hd, g, segs, s, gn);
   }
 }
 
@@ -875,6 +1125,38 @@ hipError_t launch_chunkwise_mfma(const void* q, const void* k, const void* v, co
   }
   if (zs) return launch_fwd_ct<128, true>(pp, B, H, T, dk, dv, C, hd, g, segs, s);
   return launch_fwd_ct<128, false>(pp, B, H, T, dk, dv, C, hd, g, segs, s);
+}
+
+size_t chunkwise_gn_record_bytes(int B, int H, int T, int dv, int C) {
+  const ChunkSegments sg = chunkwise_mfma_segments(B, H, T, dv, C);
+  return static_cast<size_t>(sg.nseg) * B * H * (dv / kTN) * static_cast<size_t>(sg.seg_len) * 8u;
+}
+
+bool chunkwise_gn_supports(int B, int H, int T, int dv, int C) {
+  const ChunkSegments sg = chunkwise_mfma_segments(B, H, T, dv, C);
+  // 8 tiles at most (two records per lane); one head's records within the
+  // 32-bit offsets of a buffer resource
+  return dv / kTN <= 8 && static_cast<long>(dv / kTN) * sg.seg_len * 8 < (1L << 31);
+}
+
+hipError_t launch_chunkwise_mfma_gn(const void* q, const void* k, const void* v, const float* state_in,
+                                    float* state_out, void* y, int B, int H, int T, int dk, int dv, int C,
+                                    const ChunkSegments& segs, float* ws, const GnLaunch& gl, const HeadGroup& g,
+                                    hipStream_t s) {
+  const HeadDecay hd = make_head_decay(g);
+  const PassPtrs p{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                   state_in, state_out, static_cast<uint16_t*>(y), 0, 0, ws};
+  const PassPtrs pp[2] = {p, p};
+  const GnArgs gn{gl.weight, gl.bias, gl.eps, static_cast<unsigned long long*>(gl.records), gl.err, B, H,
+                  gl.spin_limit, 0};
+  const int ct = C <= 64 ? 64 : 128;
+  const bool zs = zeta_staged(hd, g.nh, ct - 1);
+  if (C <= 64) {
+    if (zs) return launch_fwd_ct<64, true, true>(pp, B, H, T, dk, dv, C, hd, g, segs, s, gn);
+    return launch_fwd_ct<64, false, true>(pp, B, H, T, dk, dv, C, hd, g, segs, s, gn);
+  }
+  if (zs) return launch_fwd_ct<128, true, true>(pp, B, H, T, dk, dv, C, hd, g, segs, s, gn);
+  return launch_fwd_ct<128, false, true>(pp, B, H, T, dk, dv, C, hd, g, segs, s, gn);
 }
 
 bool chunkwise_mfma_pass_supports(int da, int dx) {

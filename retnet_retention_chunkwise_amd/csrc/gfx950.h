@@ -63,6 +63,18 @@ __device__ __forceinline__ void buffer_store16(rsrc_t r, uint32_t off, u32x4 x) 
   __builtin_amdgcn_raw_buffer_store_b128(x, r, static_cast<int>(off), 0, 0);
 }
 
+// Sum of x over the four lanes l, l^16, l^32, l^48 (the four 16-lane rows of
+// the wave at one position), in each of them: the gfx950 cross-row swaps
+// v_permlane32_swap (rows 0,1 <-> 2,3) and v_permlane16_swap (rows 0 <-> 1,
+// 2 <-> 3), VALU operations with no LDS round trip.  The two operands of each
+// addition are the same pair in all four lanes, so they agree bit for bit.
+__device__ __forceinline__ float row4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Eight fp32 values as an MFMA bf16 operand (round to nearest even).
 __device__ __forceinline__ bf16x8 pack_bf16x8(f32x4 lo, f32x4 hi) {
   bf16x8 r;

@@ -55,6 +55,25 @@ hipError_t launch_chunkwise_mfma(const void* q, const void* k, const void* v, co
                                  float* state_out, void* y, int B, int H, int T, int dk, int dv, int C,
                                  const ChunkSegments& segs, float* ws, const HeadGroup& g, hipStream_t s);
 
+// The same forward with the per-head GroupNorm fused into the output stores
+// (y receives the normalised outputs).  records: chunkwise_gn_record_bytes()
+// bytes filled with 0xFF before the launch; err: one int set to 1 if a wait
+// for another tile's records gave up after spin_limit polls.
+struct GnLaunch {
+  const float* weight;  // [H, dv] or null
+  const float* bias;    // [H, dv] or null
+  float eps;
+  void* records;
+  int* err;
+  int spin_limit;
+};
+bool chunkwise_gn_supports(int B, int H, int T, int dv, int C);
+size_t chunkwise_gn_record_bytes(int B, int H, int T, int dv, int C);
+hipError_t launch_chunkwise_mfma_gn(const void* q, const void* k, const void* v, const float* state_in,
+                                    float* state_out, void* y, int B, int H, int T, int dk, int dv, int C,
+                                    const ChunkSegments& segs, float* ws, const GnLaunch& gl, const HeadGroup& g,
+                                    hipStream_t s);
+
 // Passes of the same kernel for the gradients, in chunks of kPassChunk
 // positions: each pass runs forward in time or backwards with the decay
 // weights shifted by one token (rev = 1; position p = T-1-n for token n, chunk
@@ -149,5 +168,8 @@ hipError_t launch_short_bf16(const void* q, const void* k, const void* v, const 
 
 // Copies state_in (or zeros when null) into state_out: the T = 0 case.
 hipError_t launch_state_copy(const float* state_in, float* state_out, size_t n, hipStream_t s);
+
+// Sets n 32-bit words to val (a kernel, so that it can sit in a captured graph).
+hipError_t launch_fill_u32(void* p, size_t n, unsigned int val, hipStream_t s);
 
 }  // namespace ret

@@ -52,7 +52,7 @@ extern "C" ret_status retention_chunkwise_fwd_noalloc(const void* q, const void*
                                                       void* y, int B, int H, int T, int dk, int dv, int C,
                                                       ret_dtype dt, void* stream) {
   const ret::ChunkwiseFwdArgs a{q, k, v, gamma, state_in, state_out, y, B, H, T, dk, dv, C, static_cast<int>(dt)};
-  ret_status st = ret::chunkwise_fwd_check(a, nullptr, 0, false);
+  ret_status st = ret::chunkwise_fwd_check(a, nullptr, 0, false, "retention_chunkwise_fwd_noalloc");
   if (st != RET_OK) return st;
   const size_t need = retention_chunkwise_workspace_bytes(B, H, T, dk, dv, C, dt);
   char msg[256];

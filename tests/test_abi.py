@@ -353,3 +353,44 @@ def test_noalloc_rejects_calls_beyond_its_static_scratch(lib):
     # argument errors are reported as by retention_chunkwise_fwd
     st = lib.retention_chunkwise_fwd_noalloc(None, k, v, gam(0.5), None, None, y, 1, 1, 8, 16, 16, 4, 0, None)
     assert st == INVALID and "required" in _lib.last_error()
+
+
+def fgn(lib, q=FAKE, k=ctypes.c_void_p(0x20000000), v=ctypes.c_void_p(0x40000000), state_in=None, state_out=None,
+        w=None, b=None, eps=1e-5, y=ctypes.c_void_p(0x80000000), B=1, H=2, T=300, dk=64, dv=128, C=64, dt=1,
+        ws=None, wsb=0, g=None):
+    g = gam(0.9, 0.5) if g is None else g
+    return lib.retention_chunkwise_fwd_group_norm(q, k, v, g, state_in, state_out, w, b, ctypes.c_float(eps), y, B,
+                                                  H, T, dk, dv, C, dt, ws, wsb, None)
+
+
+def test_fused_group_norm_workspace_query(lib):
+    """The fused GroupNorm's workspace: 256 bytes, the forward's segment slots
+    (rounded up to 256 bytes) and 8 bytes per row and column tile; calls that
+    do not take the fused kernel need the forward's workspace only."""
+    q = lib.retention_chunkwise_fwd_group_norm_workspace_bytes
+    fwd = lib.retention_chunkwise_workspace_bytes
+    # layer1p3b: one segment, 8 column tiles
+    assert q(4, 8, 2048, 256, 512, 64, 1) == 256 + 4 * 8 * 8 * 2048 * 8
+    # long64k: 4 segments of 16384 positions, 16 state slots
+    assert q(1, 8, 65536, 256, 512, 128, 1) == 256 + fwd(1, 8, 65536, 256, 512, 128, 1) + 4 * 8 * 8 * 16384 * 8
+    # not fused: blocks of up to 64 tokens, fp32, dv above 512 or not a multiple of 64
+    assert q(1, 2, 64, 64, 128, 16, 1) == fwd(1, 2, 64, 64, 128, 16, 1) == 0
+    assert q(1, 2, 300, 64, 128, 64, 0) == fwd(1, 2, 300, 64, 128, 64, 0)
+    assert q(1, 2, 300, 64, 100, 64, 1) == fwd(1, 2, 300, 64, 100, 64, 1)
+    bad = ctypes.c_size_t(-1).value
+    assert q(0, 2, 300, 64, 128, 64, 1) == bad and q(1, 2, 300, 64, 128, 0, 1) == bad
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(B=0), INVALID, "retention_chunkwise_fwd_group_norm"),
+    (dict(eps=-1.0), INVALID, "eps"),
+    (dict(eps=float("inf")), INVALID, "eps"),
+    (dict(w=FAKE_MIS), UNSUPPORTED, "aligned"),
+    (dict(w=ctypes.c_void_p(0x80000000 + 4096)), INVALID, "weight or bias"),
+    (dict(), INVALID, "workspace"),                                 # the fused call needs its records
+    (dict(ws=ctypes.c_void_p(0xC0000000), wsb=64), INVALID, "workspace"),
+    (dict(ws=ctypes.c_void_p(0x80000000 + 8192), wsb=1 << 20), INVALID, "workspace overlaps"),
+])
+def test_fused_group_norm_rejects(lib, kw, status, needle):
+    assert fgn(lib, **kw) == status
+    assert needle in _lib.last_error(), _lib.last_error()
