@@ -556,6 +556,7 @@ def main():
         out["config"] = {"workload": h["workload"], "global_batch": wl.B, "seq_len": wl.T,
                          "parallelism": "single GPU"}
         out["roofline"] = h["roofline"]
+        out["group_norm_fused"] = h["group_norm_fused"]
         if "cpu_baseline" in h:
             out["cpu_baseline"] = h["cpu_baseline"]
     out.update(res)

@@ -325,8 +325,8 @@ ret_status retention_chunkwise_fwd_group_norm(const void* q, const void* k, cons
   float* slots = reinterpret_cast<float*>(base + ret::kGnHead);
   void* records = base + ret::kGnHead + ret::gn_slot_bytes(B, H, T, dk, dv, C);
   const size_t rec_bytes = ret::chunkwise_gn_record_bytes(B, H, T, dv, C);
-  hipError_t e = ret::launch_fill_u32(err, 1, 0u, s);
-  if (e == hipSuccess) e = ret::launch_fill_u32(records, rec_bytes / 4, 0xFFFFFFFFu, s);
+  // records to the sentinel and the error word to 0, in one launch
+  hipError_t e = ret::launch_fill_u32(records, rec_bytes / 4, 0xFFFFFFFFu, s, reinterpret_cast<unsigned*>(err), 0u);
   if (e != hipSuccess) return hip_fail(fn, e);
   const ret::ChunkSegments segs = ret::chunkwise_mfma_segments(B, H, T, dv, C);
   // a wait for another tile's records gives up after 2^16 device-scope polls

@@ -583,6 +583,11 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
     // until it is valid or spin_limit polls have passed.
     constexpr int GQ = kGN ? F::NQ : 1;
     constexpr int GD = kGnHold;
+    // 128-token tiles with two LDS hold slots normalise chunk ci - 2 inside
+    // the d_k pass of chunk ci (its records were loaded at the end of chunk
+    // ci - 1), where the normalisation's VALU work overlaps the pass's MFMAs;
+    // otherwise chunk ci - GD is normalised at the end of chunk ci.
+    constexpr bool kGnLate = kGnLds && GD == 2;
     static_assert(!kGN || kGnLds || GD == 2, "register holds alternate two slots");
     typedef u32x2 Held[GQ][4];
     Held held[kGN && !kGnLds ? GD : 1];
@@ -708,7 +713,7 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
       const uint16_t* Kx = Ks[X];
       const uint16_t* Vx = Vs[X];
       const uint16_t* Rx = Rt[X];
-      if constexpr (kGN) gn_load(ci - GD, kFirst());
+      if constexpr (kGN && !kGnLate) gn_load(ci - GD, kFirst());
       if constexpr (kQ2) load_q(Qnext, s1, Ln);
 
       // cross-chunk term O^T = (R_i^T Q^T) diag(gamma^(j+1)); V^T P^T
@@ -753,6 +758,13 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
         rd(0, 0);
 #pragma unroll
         for (int s = 0; s < F::KS; ++s) {
+          if constexpr (kGnLate) {
+            // after the first step (later steps keep more registers live and
+            // spill; measured 354 against 367 us per layer6p7b call at the
+            // first step, 434 us with spills halfway); chunk ci - 2 holds the
+            // slot of chunk ci
+            if (s == 1) gn_finish(ci - 2, [&](int qi, int nb) { return gh_at(ci, qi, nb); });
+          }
           if (s + 1 < F::KS) rd(s + 1, (s + 1) & 1);
           const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -858,6 +870,12 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
           gm[qi] = mt;
           gq[qi] = q2;
         }
+        if constexpr (kGnLate) {
+          // the records of chunk ci - 1, for its normalisation in chunk ci + 1
+          // (loaded before this chunk's record stores, so that waiting for
+          // them does not wait for those stores)
+          gn_load(ci - 1, kFirst());
+        }
         // publish (lane group 0) with a device-scope store, which passes the
         // XCD's L2 on its way to memory.  (A plain store beside it, meant to
         // keep the line in L2 for the first reads, measured slower: 138 us
@@ -868,25 +886,34 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
           const uint32_t off = g == 0 ? rec_off(tile, ci, qi) : kOutside;
           __builtin_amdgcn_raw_buffer_store_b64(r, rrs, off, 0, 16);
         }
-        // normalise chunk ci - GD (its records were loaded at the start of
-        // this chunk), then hold this chunk's outputs in the freed slot.  No
-        // instruction moves across this point: the records' validity check
-        // would otherwise be hoisted to the start of the chunk and wait there
-        // for loads issued just before.
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (kGnLds) {
-          // (chunk ci - GD holds the slot that chunk ci takes)
-          gn_finish(ci - GD, [&](int qi, int nb) { return gh_at(ci, qi, nb); });
+        if constexpr (kGnLate) {
+          // hold this chunk's outputs (chunk ci - 2, normalised halfway
+          // through this chunk's d_k pass, freed the slot)
 #pragma unroll
           for (int qi = 0; qi < GQ; ++qi)
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) gh_at(ci, qi, nb) = hn[qi][nb];
         } else {
-          gn_finish(ci - GD, [&](int qi, int nb) { return held[slot][qi][nb]; });
+          // normalise chunk ci - GD (its records were loaded at the start of
+          // this chunk), then hold this chunk's outputs in the freed slot.
+          // No instruction moves across this point: the records' validity
+          // check would otherwise be hoisted to the start of the chunk and
+          // wait there for loads issued just before.
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (kGnLds) {
+            // (chunk ci - GD holds the slot that chunk ci takes)
+            gn_finish(ci - GD, [&](int qi, int nb) { return gh_at(ci, qi, nb); });
 #pragma unroll
-          for (int qi = 0; qi < GQ; ++qi)
+            for (int qi = 0; qi < GQ; ++qi)
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) held[slot][qi][nb] = hn[qi][nb];
+              for (int nb = 0; nb < 4; ++nb) gh_at(ci, qi, nb) = hn[qi][nb];
+          } else {
+            gn_finish(ci - GD, [&](int qi, int nb) { return held[slot][qi][nb]; });
+#pragma unroll
+            for (int qi = 0; qi < GQ; ++qi)
+#pragma unroll
+              for (int nb = 0; nb < 4; ++nb) held[slot][qi][nb] = hn[qi][nb];
+          }
         }
       } else {
         // store Y rows, 4 columns (8 bytes) per lane and block (rows past the
@@ -916,7 +943,13 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
         if (ci + 1 < nchunks) chunk(ci + 1, Qa, Qa, I1());
       }
     }
-    if constexpr (kGN) {
+    if constexpr (kGnLate) {
+      // the chunks still waiting: nchunks - 2 (its records were loaded at the
+      // end of the last chunk) and nchunks - 1
+      if (nchunks >= 2) gn_finish(nchunks - 2, [&](int qi, int nb) { return gh_at(nchunks - 2, qi, nb); });
+      gn_load(nchunks - 1, kFirst());
+      gn_finish(nchunks - 1, [&](int qi, int nb) { return gh_at(nchunks - 1, qi, nb); });
+    } else if constexpr (kGN) {
       // the chunks still waiting: nchunks - GD .. nchunks - 1
       for (int cj = max(0, nchunks - GD); cj < nchunks; ++cj) {
         gn_load(cj, kFirst());

@@ -169,7 +169,9 @@ hipError_t launch_short_bf16(const void* q, const void* k, const void* v, const 
 // Copies state_in (or zeros when null) into state_out: the T = 0 case.
 hipError_t launch_state_copy(const float* state_in, float* state_out, size_t n, hipStream_t s);
 
-// Sets n 32-bit words to val (a kernel, so that it can sit in a captured graph).
-hipError_t launch_fill_u32(void* p, size_t n, unsigned int val, hipStream_t s);
+// Sets n 32-bit words to val, and *word to word_val when word is not null (a
+// kernel, so that it can sit in a captured graph).
+hipError_t launch_fill_u32(void* p, size_t n, unsigned int val, hipStream_t s, unsigned int* word = nullptr,
+                           unsigned int word_val = 0);
 
 }  // namespace ret

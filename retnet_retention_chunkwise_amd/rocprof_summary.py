@@ -73,6 +73,13 @@ def _mean_for(entries, substr):
     return sum(vals) / len(vals), len(vals)
 
 
+def _largest_for(entries, substr):
+    vals = [v for n, v in entries if substr in n]
+    if not vals:
+        raise ValueError(f"no dispatch of a kernel matching '{substr}'")
+    return max(vals)
+
+
 def traffic(fetch_dir, write_dir, kernel, source, copy_mib, copy_substr="copy", cmd=""):
     f_entries = _per_dispatch(fetch_dir, "FETCH_SIZE")
     w_entries = _per_dispatch(write_dir, "WRITE_SIZE")
@@ -88,8 +95,10 @@ def traffic(fetch_dir, write_dir, kernel, source, copy_mib, copy_substr="copy", 
         k_write += m
         n_w.append(str(n))
     n_f, n_w = "+".join(n_f), "+".join(n_w)
-    c_fetch, _ = _mean_for(f_entries, copy_substr)
-    c_write, _ = _mean_for(w_entries, copy_substr)
+    # the calibration copy is the largest dispatch of a copy kernel (small
+    # runtime copies, e.g. device-to-host reads of a few bytes, also match)
+    c_fetch = _largest_for(f_entries, copy_substr)
+    c_write = _largest_for(w_entries, copy_substr)
     copy_bytes = copy_mib * 1024 * 1024
     f_scale = copy_bytes / (c_fetch * 1024.0)
     w_scale = copy_bytes / (c_write * 1024.0)
