@@ -300,13 +300,14 @@ def bench_fused_group_norm(wl, sets, y, st, ws, steps, warmup, stream, ms_fwd, f
     ms_sep = graph_time_ms(separate, steps, stream)
     alg = fwd_bytes + 2 * wl.H * wl.dv * 4
     gbs = alg / (ms_fused * 1e-3) / 1e9
+    traffic = load_traffic(f"chunkwise_fused_group_norm_{wl.key}_traffic.txt", os.path.join(CSRC, "chunkwise_mfma.hip"))
     return {
         "workload": "the same call with the per-head GroupNorm (affine weight and bias, eps 1e-5) of its output",
         "fused_us": ms_fused * 1e3, "forward_then_group_norm_us": ms_sep * 1e3, "forward_alone_us": ms_fwd * 1e3,
         "fused_extra_us": (ms_fused - ms_fwd) * 1e3, "separate_extra_us": (ms_sep - ms_fwd) * 1e3,
         "wait_gave_up": err,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes_per_launch": alg},
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic, "algorithmic_bytes_per_launch": alg},
     }
 
 
