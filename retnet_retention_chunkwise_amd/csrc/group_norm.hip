@@ -9,9 +9,10 @@
 // each row (token-head) is held by one wave, each lane holding its VEC-element
 // pieces in registers (one 16-byte non-temporal load per lane for bf16 rows of
 // 512; y is read once and the output is not read back here), mean
-// and variance in two passes over the registers with wave-wide butterfly
-// sums, fp32 arithmetic throughout.
+// and variance in two passes over the registers with wave-wide sums on DPP
+// and cross-row lane swaps, fp32 arithmetic throughout.
 #include "common.h"
+#include "gfx950.h"
 #include "kernels.h"
 
 namespace ret {
@@ -75,10 +76,21 @@ __device__ __forceinline__ void load_f32(const float* p, float (&x)[VEC]) {
   }
 }
 
+// Sum over the wave's 64 lanes, the same value in every lane: DPP steps
+// inside each 16-lane row (lane pairs xor 1, xor 2, then the row mirror and
+// half-row mirror, which pair quads 0+3 with 1+2), then the two cross-row
+// swaps of row4_sum.  Every addition has the same two operands in all lanes
+// that meet it, so the sums agree bit for bit; all VALU, no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ float dpp_plus(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  v = dpp_plus<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_plus<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_plus<0x140>(v);  // row_mirror
+  v = dpp_plus<0x141>(v);  // row_half_mirror
+  return row4_sum(v);
 }
 
 // Each wave normalises kRows consecutive rows; lane l holds the pieces that
@@ -86,8 +98,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 // issued before the first reduction and the rows' butterfly sums interleave.
 // Consecutive rows are consecutive tokens of one head, so the head's weight
 // and bias pieces are loaded once per wave (again only if a row starts a new
-// head).  Two rows per wave measured best on the 1.3B-layer output (27-29 us
-// for 134 MB, against 32 us with one and 31-33 us with four).
+// head).  Two rows per wave measured best on the 1.3B-layer output (25.6 us
+// for 134 MB with the DPP sums, 27.4 us with ds_bpermute butterflies; one or
+// four rows per wave 27.8 and 29.8 us; a persistent grid that loads the next
+// pair of rows while normalising the current one 30.7-31.8 us).
 constexpr int kRows = 2;
 
 template <typename E, int VEC>
