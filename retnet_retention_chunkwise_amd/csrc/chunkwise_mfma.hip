@@ -592,6 +592,10 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
     typedef u32x2 Held[GQ][4];
     Held held[kGN && !kGnLds ? GD : 1];
     unsigned long long grec[GQ][2];
+    // after a wave has given up once, its later waits poll once only: a head
+    // whose tiles cannot all be resident then fails fast (error word set)
+    // instead of waiting out the spin limit at every chunk
+    int spin_limit = gn.spin_limit;
     constexpr uint32_t kOutside = 0x80000000u;
     rsrc_t rrs = make_rsrc(nullptr, 0u);
     if constexpr (kGN) {
@@ -648,9 +652,12 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
           __builtin_amdgcn_s_sleep(2);
           gn_load(cj, kRetry());
           ok = gn_valid();
-        } while (!ok && ++spin < gn.spin_limit);
+        } while (!ok && ++spin < spin_limit);
         // the error word (device scope), written by lane 0 of a wave that gave up
-        if (!ok) __builtin_amdgcn_raw_buffer_store_b32(1, make_rsrc(gn.err, 4u), lane == 0 ? 0u : kOutside, 0, 16);
+        if (!ok) {
+          __builtin_amdgcn_raw_buffer_store_b32(1, make_rsrc(gn.err, 4u), lane == 0 ? 0u : kOutside, 0, 16);
+          spin_limit = 1;
+        }
       }
       const int L = chunk_len(cj);
       const rsrc_t ry = make_rsrc(yh + static_cast<long>(L > 0 ? first_row(t_begin + cj * C, L) : 0) * dv,
