@@ -92,14 +92,15 @@ ret_status retention_parallel_fwd(const void* q, const void* k, const void* v, c
  * T = 0 is valid: y is untouched and state_out receives state_in (or zeros).
  * The result does not depend on C beyond rounding.  Kernels, in the order the
  * call picks them: T = 1 with state_out == state_in runs the recurrent step;
+ * bf16 blocks of 1 <= T <= 64 tokens with dk % 32 == 0 and dv % 64 == 0 run
+ * as one chunk in a single streaming pass over the state on bf16 MFMA; other
  * blocks of 1 <= T <= 32 tokens with dk % 16 == 0 and dv % 64 == 0 (either
- * dtype) run as one chunk in a single streaming pass over the state on fp32
- * MFMA; other blocks of T <= 16 tokens run the same way on fp32 VALU
- * arithmetic; bf16 inputs with dk in {64,128,256} and dv % 64 == 0 run on bf16
- * MFMA with chunks of C; fp32 inputs with dk in {64,128,256} and dv in
- * {64,128,256,512} run on fp32 MFMA with 16-token chunks; every other case
- * runs on fp32 VALU arithmetic with chunks of C.  State and accumulators are
- * fp32 throughout.
+ * dtype) the same way on fp32 MFMA; other blocks of T <= 16 tokens the same
+ * way on fp32 VALU arithmetic; bf16 inputs with dk in {64,128,256} and
+ * dv % 64 == 0 run on bf16 MFMA with chunks of C; fp32 inputs with dk in
+ * {64,128,256} and dv in {64,128,256,512} run on fp32 MFMA with 16-token
+ * chunks; every other case runs on fp32 VALU arithmetic with chunks of C.
+ * State and accumulators are fp32 throughout.
  */
 ret_status retention_chunkwise_fwd(const void* q, const void* k, const void* v, const float* gamma,
                                    const float* state_in, float* state_out, void* y, int B, int H, int T,
