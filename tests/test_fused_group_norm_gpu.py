@@ -38,6 +38,9 @@ FUSED_CASES = [
     (1, 2, 3000, 128, 128, 64, "bf16", False, True, [0.995, 0.9]),           # segments, 2 column tiles
     (2, 40, 200, 64, 512, 64, "bf16", True, True, None),                     # 640 workgroups (> 256 compute units)
     (1, 2, 65, 256, 512, 64, "bf16", True, True, [0.97, 0.9]),               # shortest fused call: 2 chunks
+    (1, 130, 96, 64, 64, 32, "bf16", True, True, None),                     # 2 head groups, one column tile
+    (3, 2, 777, 128, 320, 100, "bf16", False, True, [0.95, 0.999]),         # 5 column tiles, ragged, C < tile
+    (1, 1, 9000, 64, 128, 128, "bf16", True, False, [0.9999]),              # segments, gamma near 1
     (1, 3, 129, 128, 512, 128, "bf16", False, True, [0.9, 0.99, 0.6]),       # 128-token tiles, 1-row tail
     (1, 2, 100, 64, 128, 32, "f32", True, True, [0.9, 0.99]),                # fp32: forward, then GroupNorm
     (1, 2, 64, 64, 128, 16, "bf16", True, True, [0.9, 0.99]),                # short block: forward, then GroupNorm
