@@ -130,3 +130,23 @@ def test_group_norm_random_shape(case):
                          out=yd if in_place else None)
     torch.cuda.synchronize()
     check("group norm", out, ref, tol(y.dtype))
+
+
+@pytest.mark.parametrize("case", cases(16, 2028), ids=lambda c: "B{}H{}T{}dk{}dv{}C{}{}".format(*c[:7]))
+def test_fused_group_norm_random_shape(case):
+    """The forward with the per-head GroupNorm fused in (or, for shapes the
+    fused kernel does not take, the forward followed by the standalone pass)
+    against the oracle's GroupNorm of the oracle's output."""
+    B, H, T, dk, dv, C, dt, with_in, affine, gs = case
+    say(f"fused group norm {case[:9]}")
+    q, k, v, s0 = make_inputs(B, H, T, dk, dv, dt, seed=73, with_state=True)
+    s0 = s0 if with_in else None
+    gen = torch.Generator().manual_seed(74)
+    w, b = (torch.randn(H, dv, generator=gen), torch.randn(H, dv, generator=gen)) if affine else (None, None)
+    y_ref, _ = oracle.recurrent(q, k, v, torch.tensor(gs, dtype=torch.float64), s0)
+    ref = oracle.group_norm(y_ref, w, b, 1e-5)
+    dev = lambda t: None if t is None else t.to(DEV)
+    y, _ = ret.chunkwise_fwd_group_norm(dev(q), dev(k), dev(v), gs, C, dev(w), dev(b), 1e-5, state_in=dev(s0),
+                                        state_out=False)
+    torch.cuda.synchronize()
+    check("y", y, ref, tol(q.dtype))
