@@ -241,6 +241,19 @@ ret_status retention_chunkwise_fwd_group_norm(const void* q, const void* k, cons
 size_t retention_chunkwise_fwd_group_norm_workspace_bytes(int B, int H, int T, int dk, int dv, int C, ret_dtype dt);
 
 /*
+ * Testing hook for the fused call's failure path (not for production use):
+ * sets, process-wide, the number of polls after which a wait for another
+ * tile's statistics gives up (default 65536, >= 1) and a column tile whose
+ * statistics are never published (-1, the default: none).  With a silent
+ * tile every wait of that head gives up, so the error word of
+ * retention_chunkwise_fwd_group_norm becomes 1 and y is wrong, while every
+ * workgroup still finishes.  retention_testing_gn_wait(65536, -1) restores
+ * the defaults.  Not thread-safe: no fused call may run concurrently.
+ * Errors: RET_ERR_INVALID_ARG for spin_limit < 1 or silent_tile < -1.
+ */
+ret_status retention_testing_gn_wait(int spin_limit, int silent_tile);
+
+/*
  * One recurrent (decode) step, in place on the state: S <- gamma S + k^T v,
  * then y = q S (the new state, so the current token is included).  This is the
  * recurrent form of the aimpact page ("Il meccanismo"); the baulab page

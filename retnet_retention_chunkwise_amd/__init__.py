@@ -13,6 +13,8 @@ The compute lives in hand-written HIP kernels behind a C ABI
     group_norm(y, weight=None, bias=None, eps=1e-5) -> out   (per-head GroupNorm of y)
     chunkwise_fwd_group_norm(q, k, v, gamma, C, weight=None, bias=None, eps=1e-5, ...)
         -> (y, state_out)     (the forward with the GroupNorm fused into its stores)
+    fused_group_norm_failed(workspace, B, H, T, dk, dv, C, dtype) -> bool
+        (whether a wait of that fused call gave up; its error word)
 
 Build the library with ``python -m retnet_retention_chunkwise_amd.build``.
 """
@@ -27,10 +29,12 @@ from ._lib import (  # noqa: F401
     chunkwise_fwd_group_norm,
     chunkwise_fwd_noalloc,
     chunkwise_workspace_bytes,
+    fused_group_norm_failed,
     group_norm,
     last_error,
     load,
     parallel_fwd,
     recurrent_step,
+    testing_gn_wait,
     version,
 )

@@ -30,6 +30,7 @@ SIGNATURES = {
     "retention_chunkwise_fwd_group_norm": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _i, _i,
                                                 _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "retention_chunkwise_fwd_group_norm_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "retention_testing_gn_wait": (_i, [_i, _i]),
     "retention_chunkwise_fwd_noalloc": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "retention_recurrent_step": (_i, [_vp, _vp, _vp, _fp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "retention_group_norm": (_i, [_vp, _vp, _vp, ctypes.c_float, _vp, _i, _i, _i, _i, _i, _vp]),
@@ -210,11 +211,16 @@ def chunkwise_fwd_group_norm(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
                              weight: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
                              eps: float = 1e-5, state_in: Optional[torch.Tensor] = None,
                              state_out: Union[torch.Tensor, bool, None] = True, y: Optional[torch.Tensor] = None,
-                             workspace: Optional[torch.Tensor] = None
+                             workspace: Optional[torch.Tensor] = None, check: bool = False
                              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """The chunkwise forward with the per-head GroupNorm of its output fused in
     (retention_chunkwise_fwd_group_norm): y = group_norm(chunkwise_fwd(...)).
-    weight, bias: optional fp32 [H,dv].  Returns (y, state_out)."""
+    weight, bias: optional fp32 [H,dv].  Returns (y, state_out).
+
+    The fused kernel reports a wait that gave up (the column tiles of a head
+    not all resident at once; y is then wrong) in the workspace's first 32-bit
+    word: pass a workspace and read it with fused_group_norm_failed(), or pass
+    check=True to wait for the call here and raise RuntimeError if it is set."""
     lib = load()
     B, H, T, dk, dv, dt = _qkv_shapes(q, k, v)
     if y is not None:
@@ -246,7 +252,31 @@ def chunkwise_fwd_group_norm(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
                                                   _ptr(state_out), _ptr(weight), _ptr(bias), float(eps), _ptr(y), B,
                                                   H, T, dk, dv, int(C), dt, _ptr(workspace), ws_bytes,
                                                   _stream(q.device)))
+    if check and fused_group_norm_failed(workspace, B, H, T, dk, dv, C, q.dtype):
+        raise RuntimeError("retention_chunkwise_fwd_group_norm: a workgroup gave up waiting for the statistics "
+                           "of another column tile (the tiles of a head were not all resident); y is wrong")
     return y, state_out
+
+
+def fused_group_norm_failed(workspace: Optional[torch.Tensor], B: int, H: int, T: int, dk: int, dv: int, C: int,
+                            dtype: torch.dtype) -> bool:
+    """Whether the last chunkwise_fwd_group_norm call with this workspace and
+    shape ran the fused kernel and one of its waits gave up (error word 1).
+    Waits for the current stream (it reads the word back)."""
+    lib = load()
+    dt = RET_BF16 if dtype == torch.bfloat16 else RET_F32
+    need = int(lib.retention_chunkwise_fwd_group_norm_workspace_bytes(B, H, T, dk, dv, int(C), dt))
+    plain = int(lib.retention_chunkwise_workspace_bytes(B, H, T, dk, dv, int(C), dt))
+    if workspace is None or need == plain or need == ctypes.c_size_t(-1).value:
+        return False  # the forward and the standalone GroupNorm: no error word
+    return int(workspace[:4].view(torch.int32).item()) != 0
+
+
+def testing_gn_wait(spin_limit: int = 1 << 16, silent_tile: int = -1) -> None:
+    """retention_testing_gn_wait: failure-path testing of the fused GroupNorm
+    (poll limit of its waits; a column tile that publishes no statistics).
+    The defaults restore normal operation."""
+    _check(load().retention_testing_gn_wait(int(spin_limit), int(silent_tile)))
 
 
 def chunkwise_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma, C: int,

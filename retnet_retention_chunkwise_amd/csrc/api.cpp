@@ -196,10 +196,19 @@ bool gn_fused(int B, int H, int T, int dk, int dv, int C, int dt) {
 
 // Workspace of the fused call: [error word | 256 B][segment slots][records].
 constexpr size_t kGnHead = 256;
+// a wait for another tile's records gives up after 2^16 device-scope polls
+// (about 0.1 s), sets the error word and goes on
+constexpr int kGnSpinLimit = 1 << 16;
 size_t gn_slot_bytes(int B, int H, int T, int dk, int dv, int C) {
   const size_t b = chunkwise_segment_slots(chunkwise_mfma_segments(B, H, T, dv, C)) * B * H * dk * dv * sizeof(float);
   return (b + 255) / 256 * 256;
 }
+
+// Waits of the fused kernel: polls before giving up, and a column tile whose
+// records are never published (-1: none).  Process-wide; changed only by
+// retention_testing_gn_wait.
+int g_gn_spin_limit = kGnSpinLimit;
+int g_gn_silent_tile = -1;
 
 }  // namespace ret
 
@@ -329,12 +338,19 @@ ret_status retention_chunkwise_fwd_group_norm(const void* q, const void* k, cons
   hipError_t e = ret::launch_fill_u32(records, rec_bytes / 4, 0xFFFFFFFFu, s, reinterpret_cast<unsigned*>(err), 0u);
   if (e != hipSuccess) return hip_fail(fn, e);
   const ret::ChunkSegments segs = ret::chunkwise_mfma_segments(B, H, T, dv, C);
-  // a wait for another tile's records gives up after 2^16 device-scope polls
-  // (about 0.1 s), sets the error word and goes on
-  const ret::GnLaunch gl{weight, bias, eps, records, err, 1 << 16};
+  const ret::GnLaunch gl{weight, bias, eps, records, err, ret::g_gn_spin_limit, ret::g_gn_silent_tile};
   return for_head_groups(fn, H, gamma, [&](const ret::HeadGroup& g) {
     return ret::launch_chunkwise_mfma_gn(q, k, v, state_in, state_out, y, B, H, T, dk, dv, C, segs, slots, gl, g, s);
   });
+}
+
+ret_status retention_testing_gn_wait(int spin_limit, int silent_tile) {
+  const char* fn = "retention_testing_gn_wait";
+  if (spin_limit < 1) return fail(RET_ERR_INVALID_ARG, "%s: spin_limit = %d must be >= 1", fn, spin_limit);
+  if (silent_tile < -1) return fail(RET_ERR_INVALID_ARG, "%s: silent_tile = %d must be >= -1", fn, silent_tile);
+  ret::g_gn_spin_limit = spin_limit;
+  ret::g_gn_silent_tile = silent_tile;
+  return ok();
 }
 
 size_t retention_chunkwise_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C, ret_dtype dt) {

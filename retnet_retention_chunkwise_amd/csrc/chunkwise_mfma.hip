@@ -118,6 +118,7 @@ struct GnArgs {
   int Htot;
   int spin_limit;
   int items;  // work items of the launch; the grid may be padded past them
+  int silent_tile;  // failure-path testing: this column tile publishes no records (-1: none)
 };
 constexpr unsigned long long kGnEmpty = ~0ull;
 constexpr int kGnDelay = 2;  // chunks a rounded output waits for the records
@@ -890,7 +891,7 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
 #pragma unroll
         for (int qi = 0; qi < GQ; ++qi) {
           const u32x2 r = {__float_as_uint(gm[qi]), __float_as_uint(gq[qi])};
-          const uint32_t off = g == 0 ? rec_off(tile, ci, qi) : kOutside;
+          const uint32_t off = g == 0 && tile != gn.silent_tile ? rec_off(tile, ci, qi) : kOutside;
           __builtin_amdgcn_raw_buffer_store_b64(r, rrs, off, 0, 16);
         }
         if constexpr (kGnLate) {
@@ -1190,7 +1191,7 @@ hipError_t launch_chunkwise_mfma_gn(const void* q, const void* k, const void* v,
                    state_in, state_out, static_cast<uint16_t*>(y), 0, 0, ws};
   const PassPtrs pp[2] = {p, p};
   const GnArgs gn{gl.weight, gl.bias, gl.eps, static_cast<unsigned long long*>(gl.records), gl.err, B, H,
-                  gl.spin_limit, 0};
+                  gl.spin_limit, 0, gl.silent_tile};
   const int ct = C <= 64 ? 64 : 128;
   const bool zs = zeta_staged(hd, g.nh, ct - 1);
   if (C <= 64) {

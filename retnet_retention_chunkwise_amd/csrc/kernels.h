@@ -65,7 +65,8 @@ struct GnLaunch {
   float eps;
   void* records;
   int* err;
-  int spin_limit;
+  int spin_limit;   // polls before a wait for another tile's records gives up
+  int silent_tile;  // failure-path testing: a column tile that publishes no records (-1: none)
 };
 bool chunkwise_gn_supports(int B, int H, int T, int dv, int C);
 size_t chunkwise_gn_record_bytes(int B, int H, int T, int dv, int C);

@@ -394,3 +394,13 @@ def test_fused_group_norm_workspace_query(lib):
 def test_fused_group_norm_rejects(lib, kw, status, needle):
     assert fgn(lib, **kw) == status
     assert needle in _lib.last_error(), _lib.last_error()
+
+
+def test_fused_group_norm_testing_hook_validates_and_restores(lib):
+    """retention_testing_gn_wait (host-side settings only, no HIP call)."""
+    assert lib.retention_testing_gn_wait(0, -1) == INVALID
+    assert "spin_limit" in _lib.last_error()
+    assert lib.retention_testing_gn_wait(8, -2) == INVALID
+    assert "silent_tile" in _lib.last_error()
+    assert lib.retention_testing_gn_wait(8, 1) == _lib.RET_OK
+    assert lib.retention_testing_gn_wait(1 << 16, -1) == _lib.RET_OK

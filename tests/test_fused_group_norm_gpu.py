@@ -80,6 +80,39 @@ def test_fused_group_norm_vs_oracle(B, H, T, dk, dv, C, dt, with_state, aff, gs)
     assert rel_l2(y, n2) <= 1e-2
 
 
+def test_fused_group_norm_wait_gives_up_and_reports():
+    """Failure path, forced from the host: column tile 1 publishes no
+    statistics and a wait polls at most 8 times, so every workgroup of the
+    call gives up and still finishes; the error word reports it and
+    check=True raises.  With the defaults restored the same call is correct."""
+    B, H, T, dk, dv, C = 1, 2, 640, 128, 256, 64
+    gs = [0.97, 0.9]
+    say(f"fused group norm, forced give-up: B{B} H{H} T{T} dk{dk} dv{dv} C{C}")
+    q, k, v = make_inputs(B, H, T, dk, dv, "bf16", seed=83)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    need = int(_lib.load().retention_chunkwise_fwd_group_norm_workspace_bytes(B, H, T, dk, dv, C, 1))
+    assert need > ret.chunkwise_workspace_bytes(B, H, T, dk, dv, C, torch.bfloat16)  # the fused kernel runs
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    try:
+        ret.testing_gn_wait(8, 1)
+        ret.chunkwise_fwd_group_norm(qd, kd, vd, gs, C, state_out=False, workspace=ws)
+        torch.cuda.synchronize()
+        say(f"error word after the forced give-up: {err_word(ws)}")
+        assert err_word(ws) == 1
+        assert ret.fused_group_norm_failed(ws, B, H, T, dk, dv, C, torch.bfloat16)
+        with pytest.raises(RuntimeError, match="gave up"):
+            ret.chunkwise_fwd_group_norm(qd, kd, vd, gs, C, state_out=False, workspace=ws, check=True)
+    finally:
+        ret.testing_gn_wait()
+    y, _ = ret.chunkwise_fwd_group_norm(qd, kd, vd, gs, C, state_out=False, workspace=ws, check=True)
+    torch.cuda.synchronize()
+    assert err_word(ws) == 0
+    y_ref, _ = oracle.chunkwise(q, k, v, torch.tensor(gs), C)
+    r = rel_l2(y, oracle.group_norm(y_ref, None, None, 1e-5))
+    say(f"after restoring the defaults: rel-L2 {r:.3e}")
+    assert r <= tol(q.dtype)
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("key", ["layer1p3b", "layer6p7b", "long64k"])
 def test_fused_group_norm_full_size_whole_tensor(key):
