@@ -12,7 +12,8 @@
 //     state moves with non-temporal loads/stores (it is streamed once per step
 //     and is larger than any cache, so it should not displace other lines);
 //   - the state row is updated in registers and reused for y without a
-//     re-read; the partial y of the 4 waves is summed through LDS.
+//     re-read; the partial y of the 4 waves is summed through LDS;
+//   - a workgroup requests its first state rows before it stages q and k.
 #include "common.h"
 #include "kernels.h"
 
@@ -42,14 +43,32 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(const T* __res
   const long head = static_cast<long>(b) * H + h0 + hl;
   const float g = gam.log2g[hl] == -INFINITY ? 0.0f : exp2f(gam.log2g[hl]);
 
+  const int c0 = blockIdx.x * 64 * VEC + lane * VEC;
+  const bool active = c0 < dv;  // VEC = 4 is only used when dv % 4 == 0
+  float* Sh = S + head * static_cast<long>(dk) * dv + c0;
+  float s[kRowsInFlight][VEC];
+  // rows r0, r0 + 4, ..., r0 + 4 (kRowsInFlight - 1) of this lane's columns
+  auto load_rows = [&](int r0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kRowsInFlight; ++u) {
+      const int r = r0 + kWaves * u;
+      if (r < dk) {
+        if constexpr (VEC == 4) {
+          const vf4 t = __builtin_nontemporal_load(reinterpret_cast<const vf4*>(Sh + static_cast<long>(r) * dv));
+          s[u][0] = t[0]; s[u][1] = t[1]; s[u][2] = t[2]; s[u][3] = t[3];
+        } else {
+          s[u][0] = Sh[static_cast<long>(r) * dv];
+        }
+      }
+    }
+  };
+  // the first rows are requested before the q/k staging and its barrier, so
+  // that a starting workgroup's state loads are in flight while it stages
+  if (active) load_rows(w);
   for (int i = tid; i < dk; i += kThreads) {
     qs[i] = Elem<T>::load(q, head * dk + i);
     ks[i] = Elem<T>::load(k, head * dk + i);
   }
-  __syncthreads();
-
-  const int c0 = blockIdx.x * 64 * VEC + lane * VEC;
-  const bool active = c0 < dv;  // VEC = 4 is only used when dv % 4 == 0
   float vv[VEC];
   float acc[VEC];
 #pragma unroll
@@ -57,23 +76,11 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(const T* __res
     vv[e] = active ? Elem<T>::load(v, head * dv + c0 + e) : 0.0f;
     acc[e] = 0.0f;
   }
+  __syncthreads();
 
-  float* Sh = S + head * static_cast<long>(dk) * dv + c0;
   if (active) {
     for (int r0 = w; r0 < dk; r0 += kWaves * kRowsInFlight) {
-      float s[kRowsInFlight][VEC];
-#pragma unroll
-      for (int u = 0; u < kRowsInFlight; ++u) {
-        const int r = r0 + kWaves * u;
-        if (r < dk) {
-          if constexpr (VEC == 4) {
-            const vf4 t = __builtin_nontemporal_load(reinterpret_cast<const vf4*>(Sh + static_cast<long>(r) * dv));
-            s[u][0] = t[0]; s[u][1] = t[1]; s[u][2] = t[2]; s[u][3] = t[3];
-          } else {
-            s[u][0] = Sh[static_cast<long>(r) * dv];
-          }
-        }
-      }
+      if (r0 != w) load_rows(r0);
 #pragma unroll
       for (int u = 0; u < kRowsInFlight; ++u) {
         const int r = r0 + kWaves * u;

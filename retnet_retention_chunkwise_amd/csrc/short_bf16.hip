@@ -61,6 +61,55 @@ __global__ __launch_bounds__(512) void short_bf16_kernel(const uint16_t* __restr
   const long qk0 = head * Tn * dk;
   const long v0 = head * Tn * dv;
 
+  const int c0 = blockIdx.x * 512 + 64 * w;  // this wave's 64 columns
+  const bool wact = c0 < dv;                 // waves past dv only help stage
+  const int cl = c0 + 4 * lr;
+
+  // v as B operands: step ks, strip st: tokens 32 ks + 8 g + e, column cl + st
+  bf16x8 vb[NKS][4];
+#pragma unroll
+  for (int ksp = 0; ksp < NKS; ++ksp) {
+    uint16_t vv[8][4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = 32 * ksp + 8 * g + e;
+      u32x2 x = {0u, 0u};
+      if (wact && t < Tn) x = *reinterpret_cast<const u32x2*>(v + v0 + static_cast<long>(t) * dv + cl);
+      vv[e][0] = static_cast<uint16_t>(x[0]);
+      vv[e][1] = static_cast<uint16_t>(x[0] >> 16);
+      vv[e][2] = static_cast<uint16_t>(x[1]);
+      vv[e][3] = static_cast<uint16_t>(x[1] >> 16);
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      s16x8 p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = static_cast<short>(vv[e][st]);
+      vb[ksp][st] = __builtin_bit_cast(bf16x8, p);
+    }
+  }
+
+  const float gT = gamma_pow(lg, Tn);
+  const long sb = head * static_cast<long>(dk) * dv + cl;
+  // rows d0 + 16 bk + 4 g + i of a 32-row step; r[bk][i] holds the 4 strips
+  auto load_step = [&](int d0, f32x4 (&r)[2][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (state_in != nullptr)
+          x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(
+              state_in + sb + static_cast<long>(d0 + 16 * bk + 4 * g + i) * dv));
+        r[bk][i] = x;
+      }
+  };
+  f32x4 cur[2][4], nxt[2][4];
+  // the first state rows are requested before the staging of q and k, so
+  // that they arrive while the workgroup prepares its operands
+  if (wact) load_step(0, cur);
+
   // q and k rows (zero past T), 16 bytes per thread and step
   for (int i = tid; i < NU * (dk / 8); i += nthr) {
     const int t = i / (dk / 8), d8 = i - t * (dk / 8);
@@ -101,35 +150,7 @@ __global__ __launch_bounds__(512) void short_bf16_kernel(const uint16_t* __restr
   }
   __syncthreads();
 
-  const int c0 = blockIdx.x * 512 + 64 * w;  // this wave's 64 columns
-  if (c0 >= dv) return;                      // no barrier follows
-  const int cl = c0 + 4 * lr;
-
-  // v as B operands: step ks, strip st: tokens 32 ks + 8 g + e, column cl + st
-  bf16x8 vb[NKS][4];
-#pragma unroll
-  for (int ksp = 0; ksp < NKS; ++ksp) {
-    uint16_t vv[8][4];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = 32 * ksp + 8 * g + e;
-      u32x2 x = {0u, 0u};
-      if (t < Tn) x = *reinterpret_cast<const u32x2*>(v + v0 + static_cast<long>(t) * dv + cl);
-      vv[e][0] = static_cast<uint16_t>(x[0]);
-      vv[e][1] = static_cast<uint16_t>(x[0] >> 16);
-      vv[e][2] = static_cast<uint16_t>(x[1]);
-      vv[e][3] = static_cast<uint16_t>(x[1] >> 16);
-    }
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      typedef short s16x8 __attribute__((ext_vector_type(8)));
-      s16x8 p;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = static_cast<short>(vv[e][st]);
-      vb[ksp][st] = __builtin_bit_cast(bf16x8, p);
-    }
-  }
-
+  if (!wact) return;  // no barrier follows
   f32x4 acc[NTB][4];  // (Q R)[16 tb + 4 g + i][cl + st]
 #pragma unroll
   for (int tb = 0; tb < NTB; ++tb)
@@ -137,23 +158,6 @@ __global__ __launch_bounds__(512) void short_bf16_kernel(const uint16_t* __restr
     for (int st = 0; st < 4; ++st) acc[tb][st] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (state_in != nullptr || state_out != nullptr) {
-    const float gT = gamma_pow(lg, Tn);
-    const long sb = head * static_cast<long>(dk) * dv + cl;
-    // rows d0 + 16 bk + 4 g + i of the step; r[bk][i] holds the 4 strips
-    auto load_step = [&](int d0, f32x4 (&r)[2][4]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f32x4 x = {0.f, 0.f, 0.f, 0.f};
-          if (state_in != nullptr)
-            x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(
-                state_in + sb + static_cast<long>(d0 + 16 * bk + 4 * g + i) * dv));
-          r[bk][i] = x;
-        }
-    };
-    f32x4 cur[2][4], nxt[2][4];
-    load_step(0, cur);
     for (int d0 = 0; d0 < dk; d0 += 32) {
       if (d0 + 32 < dk) load_step(d0 + 32, nxt);
       // (Q R): k slot e <-> row d0 + 16 (e/4) + 4 g + e%4
