@@ -81,6 +81,7 @@ struct SegArgs {
   int nseg;        // segments; 1 = whole sequence, ws unused
   int bnh;         // B * heads of this launch
   long ws_stride;  // elements per slot (B * H * dk * dv)
+  int nsub;        // state-only launch: sub-segments per segment (0: none skipped)
 };
 
 // Pointers of one pass (the kernel takes one or two; see kDir).
@@ -122,6 +123,10 @@ struct GnArgs {
 };
 constexpr unsigned long long kGnEmpty = ~0ull;
 constexpr int kGnDelay = 2;  // chunks a rounded output waits for the records
+
+// -log2 of the weight below which a sub-segment's end state is left out of
+// the incoming states (state-only pass, see there)
+constexpr float kNegligibleLog2 = 40.0f;
 
 // kOut = true: the full kernel (outputs and state, 4 + 4 waves).
 // kOut = false: the state-only pass, end states from zero of the segments (or
@@ -244,6 +249,29 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
   static_assert(SRR * SLD * 4 <= NB * CT * F::KLD * 2, "state staging does not fit the K buffers");
   float* const Sst = reinterpret_cast<float*>(&Ks[0][0]);
 
+  if constexpr (!kOut) {
+    // State-only pass: sub-segment j of a segment of nsub reaches every later
+    // state only through the factor gamma^d, d = (nsub - 1 - j) * sub_len, of
+    // the scan (later segments add further factors <= 1).  With gamma^d <=
+    // 2^-40 its end state, whose terms are already scaled by gamma^(positions
+    // to its own end), moves no later state by more than 2^-40 of its own
+    // size, far below the bf16 rounding of the operands and of y: the
+    // workgroup writes a zero slot instead of walking the sub-segment.  Fast
+    // decays (gamma = 1 - 2^-5 ... 1 - 2^-8: every sub-segment of 4096
+    // positions but the last one or two) leave most of the pass; gamma = 0
+    // makes every such contribution exactly zero.  The full pass still walks
+    // every position.
+    if (sg.nsub > 0) {
+      const long d = static_cast<long>(sg.nsub - 1 - seg % sg.nsub) * sg.seg_len;
+      if (static_cast<float>(d) * -lg >= kNegligibleLog2) {  // (d = 0 with gamma = 0 gives NaN: walked)
+        for (int i = tid; i < DK * (kTN / 4); i += 256) {
+          const int row = i / (kTN / 4), c4 = i % (kTN / 4);
+          *reinterpret_cast<f32x4*>(&fin[sbase + static_cast<long>(row) * dv + 4 * c4]) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        return;  // before any barrier, by the whole workgroup
+      }
+    }
+  }
   if (!kOut || w >= 4) {
     // =========================== state waves ===========================
     const int st = kOut ? tid - 256 : tid;  // staging thread index 0..255
@@ -1032,7 +1060,7 @@ hipError_t launch_cfg(const PassPtrs (&pp)[2], int npass, int B, int H, int Tn, 
     // of its ws, i.e. to the sub-segment slots
     PassPtrs pre[2] = {pp[0], pp[1]};
     for (auto& p : pre) p.ws = p.ws + (segs.nseg - 1) * stride;
-    const SegArgs sp{sub_len, nsubs + 1, bnh, stride};
+    const SegArgs sp{sub_len, nsubs + 1, bnh, stride, segs.nsub};
     if (sub_len % 64 == 0)
       hipLaunchKernelGGL((chunkwise_mfma_kernel<64, DK, false, kZS, kDir>), dim3(items * nsubs), dim3(256), 0, s,
                          pre[0], pre[1], npass, hd, H, g.h0, g.nh, Tn, dx, 64, ntiles, sp, GnArgs{});
@@ -1051,7 +1079,7 @@ hipError_t launch_cfg(const PassPtrs (&pp)[2], int npass, int B, int H, int Tn, 
       if (e != hipSuccess) return e;
     }
   }
-  const SegArgs sg{segs.seg_len, segs.nseg, bnh, stride};
+  const SegArgs sg{segs.seg_len, segs.nseg, bnh, stride, 0};
   GnArgs ga = gn;
   unsigned grid = static_cast<unsigned>(items * segs.nseg);
   if (kGN) {

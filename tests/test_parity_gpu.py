@@ -272,6 +272,32 @@ def test_segmented_bwd_in_place_and_explicit_workspace():
         check(name, g, r, 2e-2)
 
 
+def test_segmented_calls_with_negligible_sub_segments():
+    """Segmented forward and backward whose state-only pass leaves out the
+    sub-segments that reach the next segment only through gamma^d <= 2^-40.
+    B1 H5 T8192 dk64 dv64 C64: 5 walkers -> 16 segments of 512 positions, 2
+    sub-segments of 256 each in the state-only pass; the first sub-segment of a
+    segment (d = 256) is left out for gamma = 0 and 0.5 and walked for
+    1 - 2^-5, 0.999 and 1.  Both directions against the oracle."""
+    B, H, T, dk, dv, C = 1, 5, 8192, 64, 64, 64
+    gs = [0.0, 0.5, 1 - 2 ** -5, 0.999, 1.0]
+    say(f"segmented forward and backward with negligible sub-segments, gammas {gs}")
+    q, k, v, s0, dy, ds = bwd_inputs(B, H, T, dk, dv, "bf16", seed=47)
+    y_ref, s_ref = oracle.recurrent(q, k, v, torch.tensor(gs, dtype=torch.float64), s0)
+    qd, kd, vd, sd, dyd, dsd = to_dev(q, k, v, s0, dy, ds)
+    assert ret.chunkwise_workspace_bytes(B, H, T, dk, dv, C, torch.bfloat16) > 0  # segmented
+    y, s_out = ret.chunkwise_fwd(qd, kd, vd, gs, C, state_in=sd)
+    torch.cuda.synchronize()
+    for h in range(H):
+        check(f"y (gamma {gs[h]})", y[:, h], y_ref[:, h], 2e-2)
+        check(f"state (gamma {gs[h]})", s_out[:, h], s_ref[:, h], 2e-2)
+    ref = oracle.recurrent_backward(q, k, v, torch.tensor(gs, dtype=torch.float32), dy, s0, ds)
+    got = ret.chunkwise_bwd(qd, kd, vd, gs, C, dyd, state_in=sd, grad_state_out=dsd)
+    torch.cuda.synchronize()
+    for name, g, r in zip(("grad_q", "grad_k", "grad_v", "grad_state_in"), got, ref):
+        check(name, g, r, 2e-2)
+
+
 def test_chunkwise_bwd_in_place_state_gradient_and_empty_sequence():
     """grad_state_in may be the grad_state_out buffer; T = 0 copies it through."""
     B, H, T, dk, dv = 1, 2, 50, 32, 64
