@@ -124,9 +124,22 @@ struct GnArgs {
 constexpr unsigned long long kGnEmpty = ~0ull;
 constexpr int kGnDelay = 2;  // chunks a rounded output waits for the records
 
-// -log2 of the weight below which a sub-segment's end state is left out of
-// the incoming states (state-only pass, see there)
-constexpr float kNegligibleLog2 = 40.0f;
+// Sub-segment j (of nsub, sub_len positions each) of a segment reaches every
+// later state only through the factor gamma^d, d = (nsub - 1 - j) * sub_len,
+// of the segment scan (later segments add further factors <= 1).  With
+// gamma^d <= 2^-40 its end state, whose terms are already scaled by gamma^(positions
+// to its own end), moves no later state by more than 2^-40 of its own size,
+// far below the bf16 rounding of the operands and of y: the state-only pass
+// does not walk it and the scan leaves it out.  Both kernels decide with this
+// one function, so that they agree bit for bit.  Fast decays leave most of
+// the pass (gamma = 1 - 2^-5 ... 1 - 2^-7: every sub-segment of 4096
+// positions but the last); gamma = 0 makes every such contribution exactly
+// zero (d > 0); d = 0 gives NaN for gamma = 0 and is walked.  The full pass
+// still walks every position.
+__device__ __forceinline__ bool sub_segment_negligible(float log2g, int nsub, int j, int sub_len) {
+  const float d = static_cast<float>(static_cast<long>(nsub - 1 - j) * sub_len);
+  return d * -log2g >= 40.0f;
+}
 
 // kOut = true: the full kernel (outputs and state, 4 + 4 waves).
 // kOut = false: the state-only pass, end states from zero of the segments (or
@@ -250,27 +263,9 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
   float* const Sst = reinterpret_cast<float*>(&Ks[0][0]);
 
   if constexpr (!kOut) {
-    // State-only pass: sub-segment j of a segment of nsub reaches every later
-    // state only through the factor gamma^d, d = (nsub - 1 - j) * sub_len, of
-    // the scan (later segments add further factors <= 1).  With gamma^d <=
-    // 2^-40 its end state, whose terms are already scaled by gamma^(positions
-    // to its own end), moves no later state by more than 2^-40 of its own
-    // size, far below the bf16 rounding of the operands and of y: the
-    // workgroup writes a zero slot instead of walking the sub-segment.  Fast
-    // decays (gamma = 1 - 2^-5 ... 1 - 2^-8: every sub-segment of 4096
-    // positions but the last one or two) leave most of the pass; gamma = 0
-    // makes every such contribution exactly zero.  The full pass still walks
-    // every position.
-    if (sg.nsub > 0) {
-      const long d = static_cast<long>(sg.nsub - 1 - seg % sg.nsub) * sg.seg_len;
-      if (static_cast<float>(d) * -lg >= kNegligibleLog2) {  // (d = 0 with gamma = 0 gives NaN: walked)
-        for (int i = tid; i < DK * (kTN / 4); i += 256) {
-          const int row = i / (kTN / 4), c4 = i % (kTN / 4);
-          *reinterpret_cast<f32x4*>(&fin[sbase + static_cast<long>(row) * dv + 4 * c4]) = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        return;  // before any barrier, by the whole workgroup
-      }
-    }
+    // a negligible sub-segment (see sub_segment_negligible): nothing to walk,
+    // its slot is neither written here nor read by the scan
+    if (sg.nsub > 0 && sub_segment_negligible(lg, sg.nsub, seg % sg.nsub, sg.seg_len)) return;
   }
   if (!kOut || w >= 4) {
     // =========================== state waves ===========================
@@ -1034,9 +1029,12 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ w
     float s = state_in != nullptr ? state_in[src] : 0.0f;
     ws[off] = s;
     for (int m = 1; m < nseg; ++m) {
-      // the sub-slot loads do not depend on s: unrolled, several are in flight
+      // the sub-slot loads do not depend on s: unrolled, several are in flight;
+      // negligible sub-segments were not walked and their slots are not read
 #pragma unroll 4
-      for (int j = 0; j < nsub; ++j) s = fmaf(gs, s, sub[((m - 1) * nsub + j) * stride + off]);
+      for (int j = 0; j < nsub; ++j)
+        s = sub_segment_negligible(gam.log2g[hl], nsub, j, sub_len) ? gs * s
+                                                                     : fmaf(gs, s, sub[((m - 1) * nsub + j) * stride + off]);
       ws[m * stride + off] = s;
     }
   }
