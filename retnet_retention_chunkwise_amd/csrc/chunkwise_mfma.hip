@@ -1028,13 +1028,17 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ w
     const long src = state_in_t ? head * per_head + (within % dx) * (per_head / dx) + within / dx : off;
     float s = state_in != nullptr ? state_in[src] : 0.0f;
     ws[off] = s;
+    // sub-segments 0..j0-1 of every segment are negligible (the test is
+    // monotone in j, and j = nsub - 1 never is): they were not walked, and
+    // their slots are not read
+    int j0 = 0;
+    while (j0 < nsub - 1 && sub_segment_negligible(gam.log2g[hl], nsub, j0, sub_len)) ++j0;
+    const float gskip = gamma_pow(gam.log2g[hl], j0 * sub_len);
     for (int m = 1; m < nseg; ++m) {
-      // the sub-slot loads do not depend on s: unrolled, several are in flight;
-      // negligible sub-segments were not walked and their slots are not read
+      if (j0 > 0) s *= gskip;
+      // the sub-slot loads do not depend on s: unrolled, several are in flight
 #pragma unroll 4
-      for (int j = 0; j < nsub; ++j)
-        s = sub_segment_negligible(gam.log2g[hl], nsub, j, sub_len) ? gs * s
-                                                                     : fmaf(gs, s, sub[((m - 1) * nsub + j) * stride + off]);
+      for (int j = j0; j < nsub; ++j) s = fmaf(gs, s, sub[((m - 1) * nsub + j) * stride + off]);
       ws[m * stride + off] = s;
     }
   }
