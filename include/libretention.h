@@ -92,9 +92,9 @@ ret_status retention_parallel_fwd(const void* q, const void* k, const void* v, c
  * T = 0 is valid: y is untouched and state_out receives state_in (or zeros).
  * The result does not depend on C beyond rounding.  A segmented call (see
  * retention_chunkwise_workspace_bytes) leaves out of the segments' incoming
- * states every sub-segment that reaches them only through a weight gamma^d
- * <= 2^-40, far below the rounding of the bf16 operands; every position's
- * output is still computed.  Kernels, in the order the
+ * states every sub-segment, and every leading run of positions of one, that
+ * reaches them only through a weight gamma^d <= 2^-40, far below the rounding
+ * of the bf16 operands; every position's output is still computed.  Kernels, in the order the
  * call picks them: T = 1 with state_out == state_in runs the recurrent step;
  * bf16 blocks of 1 <= T <= 64 tokens with dk % 32 == 0 and dv % 64 == 0 run
  * as one chunk in a single streaming pass over the state on bf16 MFMA; other

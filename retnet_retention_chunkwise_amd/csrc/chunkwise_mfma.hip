@@ -227,8 +227,24 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
   uint16_t* yh = P.y + head * Tn * dv + col0;
   const long sbase = head * static_cast<long>(DK) * dv + col0;
   const uint32_t vrow = static_cast<uint32_t>(dv) * 2u;  // bytes per V / Y row
-  const int t_begin = seg * sg.seg_len;
+  int t_begin = seg * sg.seg_len;
   const int t_end = min(Tn, t_begin + sg.seg_len);
+  if constexpr (!kOut) {
+    // State-only pass: position t of a walked sub-segment reaches the next
+    // segment's state with weight gamma^e, e = d + (t_end - 1 - t) (d as in
+    // sub_segment_negligible); positions with e * -log2(gamma) >= 40 are left
+    // out as whole sub-segments are, by starting the walk at the chunk that
+    // holds the first position with a larger weight.
+    if (sg.nsub > 0 && lg < 0.0f) {
+      const float emax = fmaxf(ceilf(40.0f / -lg) - 1.0f, 0.0f);  // largest e kept (e = 0 always)
+      const float d = static_cast<float>(static_cast<long>(sg.nsub - 1 - seg % sg.nsub) * sg.seg_len);
+      if (emax >= d && emax - d + 1.0f < static_cast<float>(t_end - t_begin)) {
+        const int keep = static_cast<int>(emax - d) + 1;  // >= 1
+        const int t0 = t_begin + (t_end - keep - t_begin) / C * C;
+        if (t0 > t_begin) t_begin = t0;
+      }
+    }
+  }
   const int nchunks = (t_end - t_begin + C - 1) / C;
   // Row addressing of the chunk at position s with L valid rows.  A buffer
   // resource starts at row first_row(s, L) and spans L rows; tile row r sits
