@@ -1027,23 +1027,33 @@ chunkwise_mfma_kernel(PassPtrs p0, PassPtrs p1, int npass, HeadDecay gam, int H,
 // 0); main slot m = the state after segments 0..m-1, composed sub-segment by
 // sub-segment: S <- gamma^sub_len S + local.  state_in_t: state_in holds each
 // head's [da x dx] state transposed.
+// VEC = 4: four consecutive elements of one head per thread (16-byte
+// accesses; per_head % 4 == 0 and state_in not transposed); VEC = 1: one.
+template <int VEC>
 __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ ws, const float* state_in,
                                                            int state_in_t, int dx, HeadDecay gam, int H, int h0,
                                                            int nh, int B, long per_head, int nseg, int nsub,
                                                            int sub_len, long stride) {
-  const long n = static_cast<long>(B) * nh * per_head;
+  typedef float vec_t __attribute__((ext_vector_type(VEC)));
+  const long n = static_cast<long>(B) * nh * per_head / VEC;
   const float* sub = ws + nseg * stride;
-  for (long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x; idx < n;
-       idx += static_cast<long>(gridDim.x) * blockDim.x) {
+  for (long iv = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x; iv < n;
+       iv += static_cast<long>(gridDim.x) * blockDim.x) {
+    const long idx = VEC * iv;
     const long bh = idx / per_head;
     const long within = idx % per_head;
     const int hl = static_cast<int>(bh % nh);
     const long head = (bh / nh) * H + h0 + hl;
     const long off = head * per_head + within;
     const float gs = gamma_pow(gam.log2g[hl], sub_len);
-    const long src = state_in_t ? head * per_head + (within % dx) * (per_head / dx) + within / dx : off;
-    float s = state_in != nullptr ? state_in[src] : 0.0f;
-    ws[off] = s;
+    vec_t s;
+    if constexpr (VEC == 1) {
+      const long src = state_in_t ? head * per_head + (within % dx) * (per_head / dx) + within / dx : off;
+      s = state_in != nullptr ? state_in[src] : 0.0f;
+    } else {
+      s = state_in != nullptr ? *reinterpret_cast<const vec_t*>(&state_in[off]) : vec_t(0.0f);
+    }
+    *reinterpret_cast<vec_t*>(&ws[off]) = s;
     // sub-segments 0..j0-1 of every segment are negligible (the test is
     // monotone in j, and j = nsub - 1 never is): they were not walked, and
     // their slots are not read
@@ -1054,8 +1064,12 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ w
       if (j0 > 0) s *= gskip;
       // the sub-slot loads do not depend on s: unrolled, several are in flight
 #pragma unroll 4
-      for (int j = j0; j < nsub; ++j) s = fmaf(gs, s, sub[((m - 1) * nsub + j) * stride + off]);
-      ws[m * stride + off] = s;
+      for (int j = j0; j < nsub; ++j) {
+        const vec_t x = *reinterpret_cast<const vec_t*>(&sub[((m - 1) * nsub + j) * stride + off]);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s[e] = fmaf(gs, s[e], x[e]);
+      }
+      *reinterpret_cast<vec_t*>(&ws[m * stride + off]) = s;
     }
   }
 }
@@ -1091,8 +1105,15 @@ hipError_t launch_cfg(const PassPtrs (&pp)[2], int npass, int B, int H, int Tn, 
     const long n = static_cast<long>(bnh) * per_head;
     const unsigned blocks = static_cast<unsigned>(min(65536L, (n + 255) / 256));
     for (int i = 0; i < npass; ++i) {
-      hipLaunchKernelGGL(segment_scan_kernel, dim3(blocks), dim3(256), 0, s, pp[i].ws, pp[i].state_in,
-                         pp[i].state_in_t, dx, hd, H, g.h0, g.nh, B, per_head, segs.nseg, segs.nsub, sub_len, stride);
+      if (!pp[i].state_in_t && per_head % 4 == 0) {
+        const unsigned b4 = static_cast<unsigned>(min(65536L, (n / 4 + 255) / 256));
+        hipLaunchKernelGGL(segment_scan_kernel<4>, dim3(b4), dim3(256), 0, s, pp[i].ws, pp[i].state_in, 0, dx, hd, H,
+                           g.h0, g.nh, B, per_head, segs.nseg, segs.nsub, sub_len, stride);
+      } else {
+        hipLaunchKernelGGL(segment_scan_kernel<1>, dim3(blocks), dim3(256), 0, s, pp[i].ws, pp[i].state_in,
+                           pp[i].state_in_t, dx, hd, H, g.h0, g.nh, B, per_head, segs.nseg, segs.nsub, sub_len,
+                           stride);
+      }
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
