@@ -584,6 +584,44 @@ def test_chunkwise_in_a_captured_graph_matches_eager():
             assert torch.equal(a, b), rep
 
 
+def test_segmented_calls_in_a_captured_graph_match_eager():
+    """Segmented forward and backward (state-only launch with negligible
+    sub-segments and positions left out, segment scan on 16-byte and on
+    single-element accesses, full launch) captured in a HIP graph give the eager
+    result bit for bit on every replay."""
+    B, H, T, dk, dv, C = 1, 5, 8192, 64, 64, 64
+    gs = [0.0, 0.5, 1 - 2 ** -5, 0.999, 1.0]
+    say("segmented forward and backward captured in a graph, replayed 3 times")
+    q, k, v, s0 = to_dev(*make_inputs(B, H, T, dk, dv, "bf16", seed=13, with_state=True))
+    dy = torch.randn(B, H, T, dv, device=DEV).div_(16).to(torch.bfloat16)
+    nf = ret.chunkwise_workspace_bytes(B, H, T, dk, dv, C, torch.bfloat16)
+    nb = int(ret.load().retention_chunkwise_bwd_workspace_bytes(B, H, T, dk, dv, C, 1))
+    assert nf > 0 and nb > 0
+    wf = torch.empty(nf, dtype=torch.uint8, device=DEV)
+    wb = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    y_eager, s_eager = ret.chunkwise_fwd(q, k, v, gs, C, state_in=s0, workspace=wf)
+    g_eager = ret.chunkwise_bwd(q, k, v, gs, C, dy, state_in=s0, workspace=wb)
+    y = torch.empty_like(y_eager)
+    s = torch.empty_like(s_eager)
+    gsi = torch.empty_like(s0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ret.chunkwise_fwd(q, k, v, gs, C, state_in=s0, state_out=s, y=y, workspace=wf)
+        out = ret.chunkwise_bwd(q, k, v, gs, C, dy, state_in=s0, grad_state_in=gsi, workspace=wb)
+    for rep in range(3):
+        y.zero_()
+        s.zero_()
+        gsi.zero_()
+        wf.zero_()
+        graph.replay()
+        other, _ = ret.chunkwise_fwd(k, q, v, gs, C)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager) and torch.equal(s, s_eager), rep
+        for a, b in zip(out, g_eager):
+            assert torch.equal(a, b), rep
+
+
 # ------------------------------------------------------- full-size workloads
 def sampled_heads(B, H):
     return sorted({(0, 0), (B // 2, H // 2), (B - 1, H - 1)})
